@@ -1,0 +1,203 @@
+/*
+ * CPU oracle for the fp16 GEMM  D = A·Bᵀ  (test infrastructure only).
+ *
+ * Only the tests, the package's smoke check and the benchmark's CPU-baseline
+ * leg may load this file's library.  It shares no code, header or table with
+ * the GPU library and never calls into it.
+ *
+ * What it computes (the plain definition, no blocking or reordering):
+ *   - "TIRx 与高性能GEMM (上)", section "从 GEMM 公式到数据路径": D = A·Bᵀ with
+ *     A of shape M×K, B of shape N×K (weight storage, so the transpose moves
+ *     no data) and D of shape M×N.
+ *   - "TIRx 基础", the closing 128×128×64 reference kernel: fp16 operands and
+ *     output with a float32 accumulator type; "TIRx Compiler Foundation",
+ *     section "Example: A GEMM Kernel": the epilogue converts with cvt.rn,
+ *     i.e. round-to-nearest-even to binary16.
+ * The oracle sums the exact fp16 products in float64 in increasing k and
+ * rounds that float64 sum straight to binary16 (never through float32, which
+ * would round twice).  Alongside it returns bound[i,j] = Σ_k |A_ik|·|B_jk|,
+ * the scale of the accumulation error any fp32 summation order can make.
+ *
+ * Layout: A[i,k] = A[i*lda + k], B[j,k] = B[j*ldb + k], row-major, leading
+ * dimensions in elements.  Outputs are dense (rows × N).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* binary16 → float64, exact.  Sign bit 15, exponent bits 14..10 (bias 15),
+ * fraction bits 9..0; exponent 0 is the subnormal range f·2^-24. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x400), e - 25);
+    return sign ? -v : v;
+}
+
+/* float64 → binary16 with round-to-nearest, ties to even, taken directly
+ * from the float64 value.  Overflow goes to ±inf (RNE rounds 65520 and above
+ * up to infinity), NaN stays NaN, subnormals are kept. */
+uint16_t oracle_double_to_half(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7e00);
+    double a = fabs(x);
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7c00);
+    if (a == 0.0)
+        return sign;
+    int e;
+    (void)frexp(a, &e);                 /* a in [2^(e-1), 2^e) */
+    int E = e - 1;                      /* unbiased exponent of a */
+    int qexp = (E >= -14) ? E - 10 : -24; /* exponent of one fp16 ulp at a */
+    double scaled = ldexp(a, -qexp);    /* exact: power-of-two scaling */
+    double fl = floor(scaled);
+    double frac = scaled - fl;          /* exact */
+    uint64_t n = (uint64_t)fl;
+    if (frac > 0.5 || (frac == 0.5 && (n & 1)))
+        n += 1;
+    if (E >= -14) {
+        /* normal binade: n in [1024, 2048] */
+        if (n == 2048) {
+            n = 1024;
+            qexp += 1;
+        }
+        int biased = qexp + 10 + 15;
+        if (biased >= 31)
+            return (uint16_t)(sign | 0x7c00);
+        return (uint16_t)(sign | (biased << 10) | (uint16_t)(n - 1024));
+    }
+    /* subnormal range: n in [0, 1024]; n == 1024 is the smallest normal,
+     * whose bit pattern is exactly 0x0400. */
+    return (uint16_t)(sign | n);
+}
+
+void oracle_half_to_double_array(const uint16_t *h, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_half_to_double(h[i]);
+}
+
+void oracle_double_to_half_array(const double *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_double_to_half(x[i]);
+}
+
+struct job {
+    const uint16_t *A, *B;
+    uint16_t *D;
+    double *bound, *sum;
+    int64_t N, K, lda, ldb;
+    const int64_t *rows;
+    int64_t nrows;
+    int64_t r_begin, r_end;
+    const double *lut;
+};
+
+static void *run_rows(void *p)
+{
+    struct job *jb = (struct job *)p;
+    for (int64_t r = jb->r_begin; r < jb->r_end; ++r) {
+        int64_t i = jb->rows ? jb->rows[r] : r;
+        const uint16_t *a = jb->A + i * jb->lda;
+        for (int64_t j = 0; j < jb->N; ++j) {
+            const uint16_t *b = jb->B + j * jb->ldb;
+            double s = 0.0, bnd = 0.0;
+            for (int64_t k = 0; k < jb->K; ++k) {
+                double x = jb->lut[a[k]];
+                double y = jb->lut[b[k]];
+                s += x * y;           /* fp16·fp16 is exact in fp64 */
+                bnd += fabs(x) * fabs(y);
+            }
+            int64_t o = r * jb->N + j;
+            if (jb->D)
+                jb->D[o] = oracle_double_to_half(s);
+            if (jb->sum)
+                jb->sum[o] = s;
+            if (jb->bound)
+                jb->bound[o] = bnd;
+        }
+    }
+    return NULL;
+}
+
+/*
+ * Reference GEMM.  Computes rows `rows[0..nrows)` of D (all M rows, in order,
+ * when rows == NULL, in which case nrows must equal M).  Output row r goes to
+ * D[r*N .. r*N+N), likewise for bound and sum (each may be NULL).  Work is
+ * split over `nthreads` POSIX threads by output row; each element's sum is
+ * taken in increasing k, so results do not depend on the thread count.
+ * Returns 0, or -1 on invalid arguments.
+ */
+int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
+                    double *bound, double *sum,
+                    int64_t M, int64_t N, int64_t K,
+                    int64_t lda, int64_t ldb,
+                    const int64_t *rows, int64_t nrows, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || nrows < 0)
+        return -1;
+    if (!rows && nrows != M)
+        return -1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= M)
+                return -1;
+    if (nrows == 0 || N == 0)
+        return 0;
+
+    double *lut = (double *)malloc(65536 * sizeof(double));
+    if (!lut)
+        return -1;
+    for (uint32_t h = 0; h < 65536; ++h)
+        lut[h] = oracle_half_to_double((uint16_t)h);
+
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > nrows)
+        nthreads = (int)nrows;
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    struct job *jobs = (struct job *)calloc((size_t)nthreads, sizeof(struct job));
+    if (!th || !jobs) {
+        free(lut);
+        free(th);
+        free(jobs);
+        return -1;
+    }
+    int64_t per = nrows / nthreads, extra = nrows % nthreads, start = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        int64_t cnt = per + (t < extra ? 1 : 0);
+        struct job jb = {A, B, D, bound, sum, N, K, lda, ldb, rows, nrows,
+                         start, start + cnt, lut};
+        jobs[t] = jb;
+        start += cnt;
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, run_rows, &jobs[t]) != 0)
+            break;
+        started = t;
+    }
+    run_rows(&jobs[0]);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(th[t], NULL);
+    /* any job whose thread could not start runs here */
+    for (int t = started + 1; t < nthreads; ++t)
+        run_rows(&jobs[t]);
+    free(lut);
+    free(th);
+    free(jobs);
+    return 0;
+}

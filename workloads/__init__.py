@@ -1,0 +1,128 @@
+"""Seeded synthetic inputs for the fp16 GEMM D = A·Bᵀ.
+
+This module only draws numbers; it holds none of the GEMM arithmetic and is
+shared by the CPU oracle's tests, the GPU parity tests, ``smoke()`` and the
+benchmark, so that both sides of every comparison see the same operands.
+
+Shapes and value distributions follow the five workloads this library is
+measured on (a single 128×128×64 tile, a ragged 1000³ case, a 4096³ square,
+an 8192×14336×4096 linear layer and a 64×28672×8192 decode-like skinny
+product).  Values are sampled in float64 with PCG64 and rounded to binary16
+with round-to-nearest-even (numpy's ``astype(np.float16)``).
+
+Reading of "N(0, 1/K)": the second parameter is the variance, so the weights
+have standard deviation 1/sqrt(K).  "N(0,1)/4" is a standard normal divided
+by four.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+SEED_A_BASE = 1000
+SEED_B_BASE = 2000
+SEED_ROWS_BASE = 3000
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    M: int
+    N: int
+    K: int
+    dist_a: tuple  # ("uniform", lo, hi) | ("normal", mean, std)
+    dist_b: tuple
+
+    @property
+    def flop(self) -> int:
+        """Algorithmic flop count 2·M·N·K (a multiply and an add per term)."""
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def min_bytes(self) -> int:
+        """Compulsory HBM bytes: read A and B once, write D once (fp16)."""
+        return 2 * (self.M * self.K + self.N * self.K + self.M * self.N)
+
+
+WORKLOADS = [
+    Workload(0, "single_tile_128x128x64", 128, 128, 64,
+             ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0)),
+    Workload(1, "ragged_1000x1000x1000", 1000, 1000, 1000,
+             ("normal", 0.0, 1.0), ("normal", 0.0, 1.0)),
+    Workload(2, "square_4096x4096x4096", 4096, 4096, 4096,
+             ("normal", 0.0, 0.25), ("normal", 0.0, 0.25)),
+    Workload(3, "linear_8192x14336x4096", 8192, 14336, 4096,
+             ("normal", 0.0, 1.0), ("normal", 0.0, 1.0 / np.sqrt(4096.0))),
+    Workload(4, "skinny_64x28672x8192", 64, 28672, 8192,
+             ("normal", 0.0, 1.0), ("normal", 0.0, 1.0 / np.sqrt(8192.0))),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def _draw(rng: np.random.Generator, shape, dist) -> np.ndarray:
+    kind = dist[0]
+    if kind == "uniform":
+        x = rng.uniform(dist[1], dist[2], size=shape)
+    elif kind == "normal":
+        x = rng.standard_normal(size=shape) * dist[2] + dist[1]
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return x.astype(np.float16)
+
+
+def make_inputs(w: Workload, lda: Optional[int] = None, ldb: Optional[int] = None):
+    """Return (A, B) as float16 arrays of shape (M, lda) and (N, ldb).
+
+    The logical operands are A[:, :K] and B[:, :K]; padding columns (when
+    lda > K or ldb > K) are filled with NaN so that any read past K shows up
+    as NaN in D.
+    """
+    lda = w.K if lda is None else lda
+    ldb = w.K if ldb is None else ldb
+    a = _draw(np.random.Generator(np.random.PCG64(SEED_A_BASE + w.index)), (w.M, w.K), w.dist_a)
+    b = _draw(np.random.Generator(np.random.PCG64(SEED_B_BASE + w.index)), (w.N, w.K), w.dist_b)
+    if lda != w.K:
+        a = pad_columns(a, lda)
+    if ldb != w.K:
+        b = pad_columns(b, ldb)
+    return a, b
+
+
+def pad_columns(x: np.ndarray, ld: int, fill=np.nan) -> np.ndarray:
+    """Copy a (rows, K) fp16 matrix into a (rows, ld) buffer, padding with ``fill``."""
+    rows, k = x.shape
+    if ld < k:
+        raise ValueError("leading dimension smaller than the row length")
+    out = np.full((rows, ld), fill, dtype=np.float16)
+    out[:, :k] = x
+    return out
+
+
+def sample_rows(w: Workload, count: int = 64) -> np.ndarray:
+    """Rows of D checked for the large workloads: ``count`` seeded random rows
+    (without replacement) plus the first and last row, sorted and unique."""
+    rng = np.random.default_rng(SEED_ROWS_BASE + w.index)
+    picked = rng.choice(w.M, size=min(count, w.M), replace=False)
+    rows = np.unique(np.concatenate([picked, [0, w.M - 1]]))
+    return rows.astype(np.int64)
+
+
+def random_f16(seed: int, shape, dist=("normal", 0.0, 1.0)) -> np.ndarray:
+    """Small helper for ad-hoc seeded operands (edge-case tests)."""
+    return _draw(np.random.Generator(np.random.PCG64(seed)), shape, dist)
+
+
+def index_pattern(M: int, N: int, K: int):
+    """Integer-valued operands whose products are exact in fp32 and fp16 for
+    K <= 341: A[i,k] = ((i + 2k) mod 5) - 2 and B[j,k] = ((3j + k) mod 7) - 3,
+    so |D| <= 6K.  Any swapped fragment, swizzle or tile offset changes D."""
+    i = np.arange(M)[:, None]
+    j = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    a = (((i + 2 * k) % 5) - 2).astype(np.float16)
+    b = (((3 * j + k) % 7) - 3).astype(np.float16)
+    return a, b
