@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp16 GEMM D = A·Bᵀ on one MI355X.
+
+One step is one tg_gemm_f16 call over the whole workload (the entire hot
+path: operand loads, LDS staging, MFMA contraction, epilogue).  Default
+workload: the 8192×14336×4096 linear-layer shape with A ~ N(0,1) and
+B ~ N(0,1/K), seeded and synthetic, resident in HBM before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+
+Prints ONE JSON line on stdout.  Timing: W untimed calls, a device
+synchronize, then K calls bracketed by HIP events recorded on the stream the
+kernel is launched on (torch's current stream), then a synchronize.  Two
+operand/output sets alternate between calls so consecutive launches do not
+find their operands in the last-level cache from the previous call.
+
+The CPU baseline is the oracle (plain C, fp64) timed on a bounded sample of
+the same workload — a prefix of D's rows, all columns, full K — on every
+host core this process may use.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+KERNEL_SOURCES = [os.path.join(ROOT, "dense_fp16_gemm_02_amd", "csrc", f)
+                  for f in ("tg_gemm.hip", "tile_layout.hpp")]
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary for
+    this kernel and workload, or None when there is none or the kernel
+    source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}__{workload}__traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_workload(w, steps: int, warmup: int, rotate: int = 2):
+    import numpy as np
+    import torch
+
+    import dense_fp16_gemm_02_amd as tg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    a, b = workloads.make_inputs(w)
+    A0 = torch.from_numpy(a).to(dev)
+    B0 = torch.from_numpy(b).to(dev)
+    sets = []
+    for r in range(rotate):
+        A = A0 if r == 0 else A0.clone()
+        B = B0 if r == 0 else B0.clone()
+        D = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+        sets.append((A, B, D))
+    stream = torch.cuda.current_stream(dev)
+    st, kname, grid = tg.tg_gemm_f16_plan(A0, B0, sets[0][2], w.M, w.N, w.K, w.K, w.K, w.N)
+    if st != tg.TG_OK:
+        raise RuntimeError(tg.tg_status_string(st))
+
+    def step(i):
+        A, B, D = sets[i % rotate]
+        s = tg.tg_gemm_f16(A, B, D, w.M, w.N, w.K, w.K, w.K, w.N, stream)
+        if s != tg.TG_OK:
+            raise RuntimeError(f"tg_gemm_f16: {tg.tg_status_string(s)}")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    del sets, A0, B0
+    torch.cuda.empty_cache()
+    return dict(ms=ms, wall_s=wall, kernel=kname, grid=grid, a=a, b=b)
+
+
+def cpu_baseline(w, a, b, seconds: float, rows_override=None):
+    """Time the oracle on the first R rows of D (all N columns, full K)."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    if rows_override:
+        R = min(rows_override, w.M)
+    else:
+        probe = min(max(1, threads), w.M)
+        t0 = time.perf_counter()
+        oracle.gemm(a, b, w.M, w.N, w.K, rows=np.arange(probe), nthreads=threads)
+        per_row = (time.perf_counter() - t0) / probe
+        R = int(min(w.M, max(threads, seconds / max(per_row, 1e-9))))
+        R = max(threads, (R // threads) * threads) if R >= threads else R
+    rows = np.arange(R, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm(a, b, w.M, w.N, w.K, rows=rows, nthreads=threads)
+    t = time.perf_counter() - t0
+    flop = 2.0 * R * w.N * w.K
+    return {
+        "value": flop / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{R - 1} of D ({R} of {w.M} rows, all {w.N} columns, K={w.K}); "
+                  f"{t:.2f} s wall",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="linear_8192x14336x4096")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target length of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=None, help="fixed oracle sample size in rows")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every workload and print a table on stderr")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this GEMM runs on one GPU; multi-GPU runs are not part of this "
+              f"build (asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    w = workloads.BY_NAME[args.workload]
+
+    if args.all:
+        log(f"{'workload':28s} {'kernel':32s} {'us':>9s} {'TFLOP/s':>9s} {'%peak':>7s} {'GB/s':>8s}")
+        for ww in workloads.WORKLOADS:
+            r = time_workload(ww, args.steps, args.warmup)
+            tf = ww.flop / (r["ms"] * 1e-3) / 1e12
+            gbs = ww.min_bytes / (r["ms"] * 1e-3) / 1e9
+            log(f"{ww.name:28s} {r['kernel']:32s} {r['ms'] * 1e3:9.2f} {tf:9.1f} "
+                f"{100 * tf / PEAK_FP16_TFLOPS:7.2f} {gbs:8.0f}")
+
+    r = time_workload(w, args.steps, args.warmup)
+    ms = r["ms"]
+    tflops = w.flop / (ms * 1e-3) / 1e12
+    log(f"{w.name}: {r['kernel']} grid={r['grid']} {ms * 1e3:.2f} us/launch "
+        f"{tflops:.1f} TFLOP/s ({100 * tflops / PEAK_FP16_TFLOPS:.1f}% of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, r["a"], r["b"], args.cpu_seconds, args.cpu_rows)
+        log(f"cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
+
+    traffic = measured_traffic(r["kernel"], w.name)
+    line = {
+        "metric": "TFLOP/s fp16 GEMM D=A·B^T at 8192x14336x4096; % of MFMA dense fp16 peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "kernel": r["kernel"],
+                   "grid": r["grid"], "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,129 @@
+"""Python binding of libtg_gemm.so — the MI355X (gfx950) fp16 GEMM D = A·Bᵀ.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``csrc/tg_gemm.hip``.  There is no fallback: if the library is
+not built, importing the functions below raises.
+
+    tg_gemm_f16(A, B, D, M, N, K, lda, ldb, ldd, stream) -> status
+    tg_gemm_f16_plan(A, B, D, M, N, K, lda, ldb, ldd) -> (status, name, grid)
+    tg_status_string(status) -> str
+    gemm(A, B, out=None, stream=None) -> D   (torch convenience wrapper)
+
+Pointers may be given as torch tensors (their ``data_ptr()``) or integers;
+``stream`` may be a ``torch.cuda.Stream``, an integer hipStream_t or None
+(the null stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_ERR_TOO_LARGE",
+           "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_status_string",
+           "gemm"]
+
+TG_OK = 0
+TG_ERR_INVALID_ARG = -1
+TG_ERR_LAUNCH = -2
+TG_ERR_DEVICE = -3
+TG_ERR_TOO_LARGE = -4
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libtg_gemm.so")
+_lib = None
+
+
+class TgError(RuntimeError):
+    def __init__(self, status: int, what: str = "tg_gemm_f16"):
+        self.status = status
+        super().__init__(f"{what} failed: {tg_status_string(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libtg_gemm.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m dense_fp16_gemm_02_amd.build` "
+            "(hipcc, gfx950) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    lib.tg_gemm_f16.restype = ctypes.c_int
+    lib.tg_gemm_f16.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    lib.tg_gemm_f16_plan.restype = ctypes.c_int
+    lib.tg_gemm_f16_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                     ctypes.c_char_p, i64, ctypes.POINTER(i64)]
+    lib.tg_status_string.restype = ctypes.c_char_p
+    lib.tg_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def tg_gemm_f16(A, B, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int, stream=None) -> int:
+    """Enqueue D ← fp16_rne(A·Bᵀ) on ``stream``; returns the C status code."""
+    return load().tg_gemm_f16(_ptr(A), _ptr(B), _ptr(D), M, N, K, lda, ldb, ldd, _stream(stream))
+
+
+def tg_gemm_f16_plan(A, B, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int):
+    """Host-only: (status, kernel name, workgroup count) tg_gemm_f16 would use."""
+    buf = ctypes.create_string_buffer(128)
+    grid = ctypes.c_int64(0)
+    st = load().tg_gemm_f16_plan(_ptr(A), _ptr(B), _ptr(D), M, N, K, lda, ldb, ldd, buf, 128,
+                                 ctypes.byref(grid))
+    return st, buf.value.decode(), grid.value
+
+
+def tg_status_string(status: int) -> str:
+    return load().tg_status_string(status).decode()
+
+
+def gemm(A, B, out=None, stream=None):
+    """torch convenience: D = A·Bᵀ for fp16 CUDA tensors A (M×K) and B (N×K)
+    whose last dimension is contiguous.  Uses torch's current stream when
+    ``stream`` is None.  Raises TgError on a non-zero status."""
+    import torch
+
+    if A.dtype != torch.float16 or B.dtype != torch.float16:
+        raise TypeError("A and B must be float16")
+    if A.dim() != 2 or B.dim() != 2 or A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A and B must be 2-D with a contiguous last dimension")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    elif out.dtype != torch.float16 or out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
+        raise ValueError("out must be a float16 (M, N) tensor with a contiguous last dimension")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    lda = A.stride(0) if M > 1 else max(K, 1)
+    ldb = B.stride(0) if N > 1 else max(K, 1)
+    ldd = out.stride(0) if M > 1 else max(N, 1)
+    st = tg_gemm_f16(A, B, out, M, N, K, max(lda, K), max(ldb, K), max(ldd, N), stream)
+    if st != TG_OK:
+        raise TgError(st)
+    return out

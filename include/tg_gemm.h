@@ -1,0 +1,96 @@
+/*
+ * tg_gemm.h — C ABI of the MI355X (gfx950) fp16 GEMM library libtg_gemm.so.
+ *
+ * The operation ("TIRx 与高性能GEMM (上)", section "从 GEMM 公式到数据路径";
+ * "TIRx 基础", the 128×128×64 reference kernel):
+ *
+ *     D = A · Bᵀ,   A: M×K,  B: N×K (weights stored row by row, so the
+ *                   transpose moves no data),  D: M×N.
+ *
+ * Operands and result are IEEE binary16; products are accumulated in fp32
+ * (the reference kernel's accumulator type) and each element of D is rounded
+ * once from fp32 to binary16 with round-to-nearest-even (the cvt.rn
+ * conversion of "TIRx Compiler Foundation", section "Example: A GEMM
+ * Kernel").  The order of the fp32 additions is unspecified.
+ *
+ * All matrices are row-major with leading dimensions in elements:
+ *     A[i,k] = A[i*lda + k],  B[j,k] = B[j*ldb + k],  D[i,j] = D[i*ldd + j].
+ *
+ * Status codes are returned by every entry point; nothing is thrown.
+ */
+#ifndef TG_GEMM_H
+#define TG_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    TG_OK = 0,
+    /* negative dimension, lda < K, ldb < K, ldd < N, or a NULL pointer for a
+     * matrix that has elements.  Nothing is launched. */
+    TG_ERR_INVALID_ARG = -1,
+    /* the HIP runtime rejected the launch (hipGetLastError after it). */
+    TG_ERR_LAUNCH = -2,
+    /* the current device is not a gfx950 GPU, or no device is usable. */
+    TG_ERR_DEVICE = -3,
+    /* a dimension or index exceeds what the kernels address (each of M, N,
+     * K, lda, ldb, ldd must be below 2^31, and A, B, D must each span fewer
+     * than 2^62 elements).  Nothing is launched. */
+    TG_ERR_TOO_LARGE = -4
+};
+
+/*
+ * tg_gemm_f16 — D ← fp16_rne(A · Bᵀ) over the M×N window of D.
+ *
+ *   A, B, D   device pointers (hipMalloc'd or equivalent) to binary16 data.
+ *             A is read over rows [0,M) and columns [0,K); B over rows [0,N)
+ *             and columns [0,K); D is written over rows [0,M) and columns
+ *             [0,N) only — elements of D outside that window, and padding
+ *             columns of A and B beyond K, are never touched.  D must not
+ *             overlap A or B (not checked).
+ *   M, N, K   problem size.  M == 0 or N == 0: returns TG_OK, nothing
+ *             launched.  K == 0: D's window is set to +0.
+ *   lda, ldb  leading dimensions of A and B in elements, >= K.
+ *   ldd       leading dimension of D in elements, >= N.
+ *   stream    a hipStream_t (NULL = the null stream).  The call only
+ *             enqueues work and returns; the caller synchronizes.
+ *
+ * There is no alpha/beta: D's prior contents are ignored.  Any alignment is
+ * accepted; 16-byte-aligned A/B with K, lda, ldb multiples of 8 take the
+ * vector-load path, other inputs a slower element-wise path with the same
+ * results.  The library allocates nothing, keeps no state between calls and
+ * is safe to call from several host threads.  Kernel faults surface at the
+ * caller's next synchronization.
+ *
+ * Returns TG_OK, TG_ERR_INVALID_ARG, TG_ERR_TOO_LARGE, TG_ERR_DEVICE or
+ * TG_ERR_LAUNCH.
+ */
+int tg_gemm_f16(const void *A, const void *B, void *D,
+                int64_t M, int64_t N, int64_t K,
+                int64_t lda, int64_t ldb, int64_t ldd,
+                void *stream);
+
+/*
+ * tg_gemm_f16_plan — host-only: the name of the kernel tg_gemm_f16 would
+ * launch for these arguments, and its grid, without touching the device.
+ * Writes a NUL-terminated name of at most `name_len` bytes into `name`
+ * (may be NULL) and the workgroup count into *grid (may be NULL; 0 when
+ * nothing would be launched).  Returns the status tg_gemm_f16 would return
+ * for argument validation (TG_OK, TG_ERR_INVALID_ARG or TG_ERR_TOO_LARGE).
+ */
+int tg_gemm_f16_plan(const void *A, const void *B, const void *D,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldd,
+                     char *name, int64_t name_len, int64_t *grid);
+
+/* tg_status_string — a static, NUL-terminated description of a status. */
+const char *tg_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_GEMM_H */

@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/*.h declares, rejects bad arguments before touching a
+device, and plans kernels for the measured workloads."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads
+
+tg = pytest.importorskip("dense_fp16_gemm_02_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(INCLUDE)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(tg_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(tg.lib_path())
+    names = declared_functions()
+    assert "tg_gemm_f16" in names and "tg_status_string" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+
+
+def test_library_is_built_for_gfx950():
+    with open(tg.lib_path(), "rb") as f:
+        blob = f.read()
+    assert b"gfx950" in blob
+
+
+FAKE = 1 << 20  # a non-NULL pointer value; validation rejects before any use
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, FAKE, FAKE, -1, 4, 4, 4, 4, 4),   # negative M
+    (FAKE, FAKE, FAKE, 4, -1, 4, 4, 4, 4),   # negative N
+    (FAKE, FAKE, FAKE, 4, 4, -1, 4, 4, 4),   # negative K
+    (FAKE, FAKE, FAKE, 4, 4, 8, 7, 8, 4),    # lda < K
+    (FAKE, FAKE, FAKE, 4, 4, 8, 8, 7, 4),    # ldb < K
+    (FAKE, FAKE, FAKE, 4, 4, 8, 8, 8, 3),    # ldd < N
+    (None, FAKE, FAKE, 4, 4, 8, 8, 8, 4),    # NULL A with elements
+    (FAKE, None, FAKE, 4, 4, 8, 8, 8, 4),    # NULL B with elements
+    (FAKE, FAKE, None, 4, 4, 8, 8, 8, 4),    # NULL D with elements
+])
+def test_invalid_arguments_rejected_without_launch(args):
+    assert tg.tg_gemm_f16(*args, None) == tg.TG_ERR_INVALID_ARG
+    st, name, grid = tg.tg_gemm_f16_plan(*args)
+    assert st == tg.TG_ERR_INVALID_ARG and name == "" and grid == 0
+
+
+def test_too_large_rejected():
+    big = 1 << 31
+    assert tg.tg_gemm_f16(FAKE, FAKE, FAKE, big, 4, 4, 4, 4, 4, None) == tg.TG_ERR_TOO_LARGE
+    assert tg.tg_gemm_f16(FAKE, FAKE, FAKE, 4, 4, 4, big, 4, 4, None) == tg.TG_ERR_TOO_LARGE
+
+
+def test_empty_problems_are_noops():
+    # M == 0 or N == 0: OK with nothing launched; matrices without elements
+    # may be NULL
+    assert tg.tg_gemm_f16(None, FAKE, None, 0, 5, 3, 3, 3, 5, None) == tg.TG_OK
+    assert tg.tg_gemm_f16(FAKE, None, None, 5, 0, 3, 3, 3, 0, None) == tg.TG_OK
+    assert tg.tg_gemm_f16(None, None, None, 0, 0, 0, 0, 0, 0, None) == tg.TG_OK
+    assert tg.tg_gemm_f16_plan(None, FAKE, None, 0, 5, 3, 3, 3, 5) == (tg.TG_OK, "", 0)
+
+
+def test_status_strings():
+    for st in (tg.TG_OK, tg.TG_ERR_INVALID_ARG, tg.TG_ERR_LAUNCH, tg.TG_ERR_DEVICE,
+               tg.TG_ERR_TOO_LARGE):
+        s = tg.tg_status_string(st)
+        assert s and s != "unknown status"
+    assert tg.tg_status_string(12345) == "unknown status"
+
+
+def test_plans_for_workloads():
+    for w in workloads.WORKLOADS:
+        st, name, grid = tg.tg_gemm_f16_plan(FAKE, FAKE, FAKE, w.M, w.N, w.K, w.K, w.K, w.N)
+        assert st == tg.TG_OK and name.startswith("gemm_f16_") and name.endswith("_vec")
+        assert grid > 0
+    # misaligned pointer or K % 8 != 0 takes the element-wise path
+    st, name, _ = tg.tg_gemm_f16_plan(FAKE + 2, FAKE, FAKE, 64, 64, 64, 64, 64, 64)
+    assert name.endswith("_scalar")
+    st, name, _ = tg.tg_gemm_f16_plan(FAKE, FAKE, FAKE, 64, 64, 60, 60, 60, 64)
+    assert name.endswith("_scalar")
+
+
+def test_binding_refuses_without_library(tmp_path, monkeypatch):
+    import importlib
+    import dense_fp16_gemm_02_amd as pkg
+    monkeypatch.setattr(pkg, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(pkg, "_lib", None)
+    with pytest.raises(ImportError):
+        pkg.load()
+    importlib.reload(pkg)
