@@ -34,20 +34,27 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+__host__ __device__ constexpr int imin(int a, int b) { return a < b ? a : b; }
+
 constexpr int BK = 64;              // K elements per LDS stage (128 bytes of fp16)
 constexpr int ROW_CHUNKS = BK / 8;  // 16-byte chunks per tile row
 
 // LDS element offset of 16-byte chunk `c` (0..7) of row `r` inside a (rows × 64)
-// fp16 tile.  This is ComposeLayout(per_element=3, swizzle_len=3, atom_len=3)
-// over TileLayout S[(rows,64):(64@m,1@m)]; the equality is checked below at
-// compile time against the layout helper.
-__host__ __device__ constexpr int lds_chunk_off(int r, int c)
-{
-    return r * BK + ((c ^ (r & 7)) << 3);
-}
+// fp16 tile: ComposeLayout(per_element=3, swizzle_len=3, atom_len=4) over
+// TileLayout S[(rows,64):(64@m,1@m)] — the pages' 128-byte swizzle keeps
+// 16-byte vectors whole and XORs the row into the chunk index; here the XOR
+// takes the row pair (r >> 1) instead of the row, because gfx950's LDS has 64
+// four-byte banks and serves a 128-bit read 16 lanes at a time: sixteen
+// consecutive rows (one MFMA fragment read's first 16 lanes) must then hit
+// sixteen different 16-byte bank groups, which the 128-byte mode misses by a
+// factor of two (rows r and r+8 collide).  Checked at compile time against
+// the layout helper.
+constexpr int SWZ_ROW_SHIFT = 1;
+__host__ __device__ constexpr int swz(int r) { return (r >> SWZ_ROW_SHIFT) & 7; }
+__host__ __device__ constexpr int lds_chunk_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
 
-static_assert(tg::layout::check_swizzled_tile(256, lds_chunk_off),
-              "LDS chunk addressing disagrees with the 128B ComposeLayout swizzle");
+static_assert(tg::layout::check_swizzled_tile(tg::layout::swizzle_pairs_f16(256), 256, lds_chunk_off),
+              "LDS chunk addressing disagrees with ComposeLayout(3, 3, 4)");
 
 // Fragment reads: lane l takes row (l & 31) and K-chunk (l >> 5) of a 32×16
 // operand slice; the epilogue reads lane l, register v as D row (l & 31) and
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_f16_kernel(
     constexpr int A_PASSES = BM / RS, B_PASSES = BN / RS;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(BM % RS == 0 && BN % RS == 0, "tile rows must be a multiple of the load pass");
-    static_assert(RS % 8 == 0, "swizzle phase must not change between load passes");
+    static_assert(RS % 16 == 0, "swizzle phase must not change between load passes");
     constexpr int STAGE = (BM + BN) * BK;
     static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS budget");
 
@@ -276,21 +283,325 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_f16_kernel(
     }
 }
 
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
+
+// One wave per SIMD is the intended occupancy of the large tiles: let the
+// scheduler spend registers on latency hiding (device compile only; the host
+// pass does not know the attribute).
+#if defined(__HIP_DEVICE_COMPILE__)
+#define TG_ONE_WAVE_PER_SIMD __attribute__((amdgpu_waves_per_eu(1, 1)))
+#else
+#define TG_ONE_WAVE_PER_SIMD
+#endif
+
+// Raw buffer descriptor word 3 for gfx9-family GPUs (32-bit data format, no
+// swizzle, no thread-id add).  Offsets at or past DMA_RANGE bytes read zeros.
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
+constexpr int DMA_RANGE = 0x7fffffff;
+constexpr uint32_t DMA_OOB = 0x80000000u;
+
+// One 16-byte-per-lane DMA: buffer bytes [voff, voff+16) of lane l land at
+// LDS bytes lds + 16·l (lds must be wave-uniform).  The builtin exists only
+// in the device pass; the host pass sees an empty body, which keeps clang
+// emitting the host-side kernel stubs.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, _Float16 *lds, uint32_t voff)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)lds, 16, voff, 0, 0, 0);
+#else
+    (void)rsrc, (void)lds, (void)voff;
+#endif
+}
+
+// The direct-to-LDS path addresses a tile with 32-bit byte offsets from its
+// origin (+k, which goes into the descriptor base): the largest offset it
+// forms, (rows-1)·ld·2 + 16·7, must stay below DMA_RANGE.
+__host__ __device__ constexpr bool dma_offsets_fit(int64_t rows, int64_t ld)
+{
+    return (rows - 1) * ld * 2 + 128 < (int64_t)DMA_RANGE;
+}
+
+__device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Main path for 16-byte aligned operands with K, lda, ldb multiples of 8 and
+// in-tile byte offsets below 2^31 (see dma_offsets_fit).
+//
+// Operand tiles move global → LDS with buffer_load_dwordx4 … lds: one wave
+// instruction fills 64 consecutive 16-byte LDS slots, i.e. eight 128-byte
+// rows — exactly one atom of the 128-byte swizzle.  The swizzle is applied
+// on the source side: lane l fills physical chunk (l & 7) of row (l >> 3),
+// so it fetches logical chunk (l & 7) ^ (l >> 3) from global memory.
+// Each DMA is a buffer descriptor whose base is the tile origin + k (in
+// SGPRs) plus a per-lane 32-bit offset fixed for the whole K loop.  (The
+// buffer form, unlike the global form, lets the compiler keep partial
+// lgkmcnt waits on the LDS fragment reads.)
+//
+// Tails: rows of A past M only feed rows of D past M, which are never
+// stored (likewise B and N), so such rows are clamped to the last valid row
+// instead of being zeroed.  Past K both operands must be exactly zero
+// (0·NaN would poison valid outputs): in the last K-tile, when K % 64 != 0,
+// lanes whose chunk lies beyond K get an offset past the descriptor's range,
+// for which the buffer unit returns zeros.
+//
+// K loop (two LDS stages, fragments double-buffered in registers):
+//   stage s holds K-tile kt; the DMA for K-tile kt+1 is in flight into s^1;
+//   K-steps 0..2: read the next K-step's fragments, then issue this step's MFMAs;
+//   wait for this wave's DMA, barrier (stage s^1 complete, stage s drained);
+//   read K-step 0 of stage s^1, issue K-step 3's MFMAs from registers, and
+//   start the DMA of K-tile kt+2 into stage s.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM *WN * 64) TG_ONE_WAVE_PER_SIMD void gemm_f16_dma_kernel(
+    const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
+    int dvec)
+{
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int A_PASSES = BM / 8 / NW, B_PASSES = BN / 8 / NW;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "row groups must split over waves");
+    constexpr int STAGE = (BM + BN) * BK;
+    static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS budget");
+
+    __shared__ __attribute__((aligned(1024))) _Float16 smem[2 * STAGE];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    // DMA source of this lane in pass p: tile row t = 8·(p·NW + wave) + (lane >> 3),
+    // whose physical chunk (lane & 7) holds logical chunk (lane & 7) ^ swz(t);
+    // byte offsets from the tile origin.  kc[p] is the logical chunk (for the
+    // K-tail test).
+    const int dr = lane >> 3;
+    uint32_t a_off[A_PASSES], b_off[B_PASSES];
+    int a_kc[A_PASSES], b_kc[B_PASSES];
+#pragma unroll
+    for (int p = 0; p < A_PASSES; ++p) {
+        const int t = 8 * (p * NW + wave) + dr;
+        a_kc[p] = (lane & 7) ^ swz(t);
+        const int r = imin(t, M - 1 - m0);
+        a_off[p] = (uint32_t)(r * lda * 2 + 16 * a_kc[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < B_PASSES; ++p) {
+        const int t = 8 * (p * NW + wave) + dr;
+        b_kc[p] = (lane & 7) ^ swz(t);
+        const int r = imin(t, N - 1 - n0);
+        b_off[p] = (uint32_t)(r * ldb * 2 + 16 * b_kc[p]);
+    }
+    const char *a_tile = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
+    const char *b_tile = reinterpret_cast<const char *>(B + (int64_t)n0 * ldb);
+
+    // DMA of K-tile kt into stage s.  Chunks past K read out of range (zeros;
+    // only the last K-tile has any); kt >= KT makes every lane out of range,
+    // a no-op copy of zeros that keeps the caller's loop free of branches.
+    auto dma = [&](int kt, int s) {
+        const int k = kt * BK;
+        const int klim = kt < (K + BK - 1) / BK ? K - k : 0;  // valid K in this tile
+        _Float16 *as = smem + s * STAGE;
+        _Float16 *bs = as + BM * BK;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a_tile + 2 * k), (short)0, DMA_RANGE, BUFFER_RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(b_tile + 2 * k), (short)0, DMA_RANGE, BUFFER_RSRC_WORD3);
+#pragma unroll
+        for (int p = 0; p < A_PASSES; ++p)
+            dma16(ra, as + (p * NW + wave) * 8 * BK, 8 * a_kc[p] < klim ? a_off[p] : DMA_OOB);
+#pragma unroll
+        for (int p = 0; p < B_PASSES; ++p)
+            dma16(rb, bs + (p * NW + wave) * 8 * BK, 8 * b_kc[p] < klim ? b_off[p] : DMA_OOB);
+    };
+
+    const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
+    f16x8 fa[2][TM], fb[2][TN];
+
+    // one fragment: q < TM is A fragment q, else B fragment q - TM
+    auto read_frag = [&](int s, int kk, int q, f16x8 *a, f16x8 *b) {
+        const _Float16 *as = smem + s * STAGE;
+        const _Float16 *bs = as + BM * BK;
+        const int c = kk * 2 + frag_hi;
+        if (q < TM)
+            a[q] = *reinterpret_cast<const f16x8 *>(as + lds_chunk_off(wm * WTM + q * 32 + frag_row, c));
+        else
+            b[q - TM] = *reinterpret_cast<const f16x8 *>(
+                bs + lds_chunk_off(wn * WTN + (q - TM) * 32 + frag_row, c));
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[i][j][v] = 0.0f;
+
+    // One K-step's TM·TN MFMAs on fragments (a, b), with the companion work
+    // pinned between them in program order (sched_barrier fences each slot):
+    // after MFMA i comes the next K-step's LDS read i (for i < TM+TN, in the
+    // order the next step first uses them: A0, B0..B(TN-1), A1..A(TM-1)) and,
+    // when `with_dma`, DMA pass i.  The matrix core runs each MFMA while the
+    // wave issues the companions; fewer than 16 LDS reads are ever in flight,
+    // so the compiler's waits stay partial.
+    constexpr int NFRAG = TM + TN;
+    // read slot i → fragment id (q < TM: A fragment q, else B fragment q - TM)
+    auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
+    auto step = [&](const f16x8 *a, const f16x8 *b, int rs, int rkk, f16x8 *na, f16x8 *nb,
+                    bool with_reads, bool with_dma, int dkt, int ds) {
+        const int k = dkt * BK;
+        const int klim = dkt < (K + BK - 1) / BK ? K - k : 0;  // valid K in that K-tile
+        _Float16 *das = smem + ds * STAGE;
+        _Float16 *dbs = das + BM * BK;
+        __amdgpu_buffer_rsrc_t ra, rb;
+        if (with_dma) {
+            ra = __builtin_amdgcn_make_buffer_rsrc((void *)(a_tile + 2 * k), (short)0, DMA_RANGE,
+                                                   BUFFER_RSRC_WORD3);
+            rb = __builtin_amdgcn_make_buffer_rsrc((void *)(b_tile + 2 * k), (short)0, DMA_RANGE,
+                                                   BUFFER_RSRC_WORD3);
+        }
+#pragma unroll
+        for (int i = 0; i < TM * TN; ++i) {
+            const int ti = i / TN, tj = i % TN;
+            acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[tj], a[ti], acc[ti][tj], 0, 0, 0);
+            if (with_reads && i < NFRAG)
+                read_frag(rs, rkk, frag_of_slot(i), na, nb);
+            if (with_dma && i < A_PASSES)
+                dma16(ra, das + (i * NW + wave) * 8 * BK, 8 * a_kc[i] < klim ? a_off[i] : DMA_OOB);
+            if (with_dma && i >= A_PASSES && i < A_PASSES + B_PASSES) {
+                const int p = i - A_PASSES;
+                dma16(rb, dbs + (p * NW + wave) * 8 * BK, 8 * b_kc[p] < klim ? b_off[p] : DMA_OOB);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // any reads left over when there are more fragments than MFMA slots
+#pragma unroll
+        for (int i = TM * TN; i < NFRAG; ++i)
+            if (with_reads)
+                read_frag(rs, rkk, frag_of_slot(i), na, nb);
+    };
+
+    // DMA of K-tile kt into stage s, passes `from` onwards, outside the MFMA
+    // stream (prologue, and shapes whose passes outnumber the MFMA slots).
+    // Chunks past K read out of range, i.e. zeros; only the last K-tile has
+    // any.  kt >= KT makes every lane out of range: a no-op copy of zeros.
+    auto dma_rest = [&](int kt, int s, int from) {
+        const int k = kt * BK;
+        const int klim = kt < (K + BK - 1) / BK ? K - k : 0;
+        _Float16 *as = smem + s * STAGE;
+        _Float16 *bs = as + BM * BK;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a_tile + 2 * k), (short)0, DMA_RANGE, BUFFER_RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(b_tile + 2 * k), (short)0, DMA_RANGE, BUFFER_RSRC_WORD3);
+#pragma unroll
+        for (int p = 0; p < A_PASSES; ++p)
+            if (p >= from)
+                dma16(ra, as + (p * NW + wave) * 8 * BK, 8 * a_kc[p] < klim ? a_off[p] : DMA_OOB);
+#pragma unroll
+        for (int p = 0; p < B_PASSES; ++p)
+            if (A_PASSES + p >= from)
+                dma16(rb, bs + (p * NW + wave) * 8 * BK, 8 * b_kc[p] < klim ? b_off[p] : DMA_OOB);
+    };
+    constexpr int DMA_IN_STREAM = (A_PASSES + B_PASSES) < TM * TN ? (A_PASSES + B_PASSES) : TM * TN;
+
+    const int KT = (K + BK - 1) / BK;
+    if (KT > 0) {
+        dma_rest(0, 0, 0);
+        wait_vmem_all();
+        __syncthreads();
+        dma_rest(1, 1, 0);  // a no-op when KT == 1
+#pragma unroll
+        for (int q = 0; q < NFRAG; ++q)
+            read_frag(0, 0, q, fa[0], fb[0]);
+    }
+    // K-steps 0..2 of the K-tile in stage s, each with the next step's reads.
+    auto first_three_steps = [&](int s) {
+#pragma unroll
+        for (int kk = 0; kk < BK / 16 - 1; ++kk)
+            step(fa[kk & 1], fb[kk & 1], s, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], true,
+                 false, 0, 0);
+    };
+    // steady state: a next K-tile exists (peeled so the loop body is straight-line)
+    for (int kt = 0; kt < KT - 1; ++kt) {
+        const int s = kt & 1;
+        first_three_steps(s);
+        wait_vmem_all();
+        __syncthreads();
+        // stage s is drained: K-step 3 runs from registers while the next
+        // stage's K-step 0 is read and stage s is refilled with K-tile kt+2
+        // (a no-op copy of zeros past the end)
+        step(fa[1], fb[1], s ^ 1, 0, fa[0], fb[0], true, true, kt + 2, s);
+        if (DMA_IN_STREAM < A_PASSES + B_PASSES)
+            dma_rest(kt + 2, s, DMA_IN_STREAM);
+    }
+    if (KT > 0) {
+        first_three_steps((KT - 1) & 1);
+        step(fa[1], fb[1], 0, 0, fa[0], fb[0], false, false, 0, 0);
+    }
+    wait_vmem_all();  // no LDS DMA may be outstanding when the wave ends
+
+    // Epilogue (same register → D map as the element-wise path).
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int row = m0 + wm * WTM + i * 32 + frag_row;
+        if (row >= M)
+            continue;
+        _Float16 *drow = D + (int64_t)row * ldd;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = n0 + wn * WTN + j * 32 + g * 8 + frag_hi * 4;
+                f16x4 h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    h[r] = (_Float16)acc[i][j][g * 4 + r];
+                if (dvec && col + 3 < N) {
+                    *reinterpret_cast<f16x4 *>(drow + col) = h;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (col + r < N)
+                            drow[col + r] = h[r];
+                }
+            }
+        }
+    }
+}
+
 struct KernelChoice {
     const void *fn;
     const char *name;
     int bm, bn, threads;
 };
 
+// Load path of a launch: direct-to-LDS DMA, 16-byte loads through registers
+// (aligned operands whose in-tile offsets exceed 32 bits), or element-wise.
+enum LoadPath { PATH_DMA = 0, PATH_VEC = 1, PATH_SCALAR = 2 };
+
 template <int BM, int BN, int WM, int WN>
-KernelChoice choice(bool vec, const char *name_vec, const char *name_scalar)
+KernelChoice choice(LoadPath path, const char *const names[3])
 {
-    if (vec)
-        return {reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, true>), name_vec,
-                BM, BN, WM * WN * 64};
-    return {reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, false>), name_scalar,
-            BM, BN, WM * WN * 64};
+    const void *fn = path == PATH_DMA
+                         ? reinterpret_cast<const void *>(&gemm_f16_dma_kernel<BM, BN, WM, WN>)
+                     : path == PATH_VEC
+                         ? reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, true>)
+                         : reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, false>);
+    return {fn, names[path], BM, BN, WM * WN * 64};
 }
+
+constexpr const char *NAMES_256[3] = {"gemm_f16_256x256_w2x2_dma", "gemm_f16_256x256_w2x2_vec",
+                                      "gemm_f16_256x256_w2x2_scalar"};
+constexpr const char *NAMES_128[3] = {"gemm_f16_128x128_w2x2_dma", "gemm_f16_128x128_w2x2_vec",
+                                      "gemm_f16_128x128_w2x2_scalar"};
+constexpr const char *NAMES_64[3] = {"gemm_f16_64x64_w2x2_dma", "gemm_f16_64x64_w2x2_vec",
+                                     "gemm_f16_64x64_w2x2_scalar"};
 
 constexpr int64_t LIMIT32 = (int64_t)1 << 31;
 constexpr int NUM_CU = 256;
@@ -321,13 +632,18 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     const bool vec = (K % 8 == 0) && (lda % 8 == 0) && (ldb % 8 == 0) &&
                      ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0);
     const auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    const auto path = [&](int bm, int bn) {
+        if (!vec)
+            return PATH_SCALAR;
+        return dma_offsets_fit(bm, lda) && dma_offsets_fit(bn, ldb) ? PATH_DMA : PATH_VEC;
+    };
     KernelChoice k;
     if (tiles(256, 256) >= NUM_CU)
-        k = choice<256, 256, 2, 2>(vec, "gemm_f16_256x256_w2x2_vec", "gemm_f16_256x256_w2x2_scalar");
+        k = choice<256, 256, 2, 2>(path(256, 256), NAMES_256);
     else if (tiles(128, 128) >= NUM_CU)
-        k = choice<128, 128, 2, 2>(vec, "gemm_f16_128x128_w2x2_vec", "gemm_f16_128x128_w2x2_scalar");
+        k = choice<128, 128, 2, 2>(path(128, 128), NAMES_128);
     else
-        k = choice<64, 64, 2, 2>(vec, "gemm_f16_64x64_w2x2_vec", "gemm_f16_64x64_w2x2_scalar");
+        k = choice<64, 64, 2, 2>(path(64, 64), NAMES_64);
     Plan p;
     p.k = k;
     p.tiles_m = (int)((M + k.bm - 1) / k.bm);

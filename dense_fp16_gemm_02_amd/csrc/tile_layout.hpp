@@ -222,6 +222,18 @@ constexpr ComposeLayout swizzle128_f16(int64_t rows)
     return ComposeLayout{Swizzle{3, 3, 3, true}, row_major(rows, 64)};
 }
 
+// The operand-tile swizzle the kernels use: ComposeLayout(3, 3, 4) over
+// S[(rows,64):(64@m,1@m)], i.e. 16-byte chunk c of row r lands at chunk
+// c ^ ((r >> 1) & 7).  Same vector-keeping M = 3 as the 128-byte mode, but the
+// XOR field comes from the row pair instead of the row: sixteen consecutive
+// rows then cover every 16-byte slot of a 256-byte bank line once, which a
+// 64-bank LDS serving 16 lanes per 128-bit read needs (the 128-byte mode
+// sends rows r and r+8 to the same banks).
+constexpr ComposeLayout swizzle_pairs_f16(int64_t rows)
+{
+    return ComposeLayout{Swizzle{3, 3, 4, true}, row_major(rows, 64)};
+}
+
 // Operand fragment of v_mfma_f32_32x32x16_f16 over a logical 32×16 (row, k)
 // tile: lane = row + 32·(k / 8), register element = k mod 8, i.e.
 // S[(32,2,8):(1@laneid,32@laneid,1@m)].
@@ -256,12 +268,10 @@ constexpr TileLayout mfma32x32_acc_swapped()
 // ------------------------------------------------------------- checks
 
 // The kernels' LDS chunk address fn(r, c) (element offset of 16-byte chunk c
-// of row r) equals the 128-byte fp16 swizzle for every element of a
-// (rows × 64) tile.
+// of row r) equals layout L for every element of a (rows × 64) tile.
 template <class F>
-constexpr bool check_swizzled_tile(int rows, F fn)
+constexpr bool check_swizzled_tile(const ComposeLayout &L, int rows, F fn)
 {
-    const ComposeLayout L = swizzle128_f16(rows);
     if (!L.well_formed())
         return false;
     for (int r = 0; r < rows; ++r)

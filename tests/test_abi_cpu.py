@@ -86,7 +86,7 @@ def test_status_strings():
 def test_plans_for_workloads():
     for w in workloads.WORKLOADS:
         st, name, grid = tg.tg_gemm_f16_plan(FAKE, FAKE, FAKE, w.M, w.N, w.K, w.K, w.K, w.N)
-        assert st == tg.TG_OK and name.startswith("gemm_f16_") and name.endswith("_vec")
+        assert st == tg.TG_OK and name.startswith("gemm_f16_") and name.endswith("_dma")
         assert grid > 0
     # misaligned pointer or K % 8 != 0 takes the element-wise path
     st, name, _ = tg.tg_gemm_f16_plan(FAKE + 2, FAKE, FAKE, 64, 64, 64, 64, 64, 64)

@@ -159,3 +159,35 @@ def test_mfma_fragment_specs_parse_as_documented():
             assert r == 8 * (v // 4) + 4 * (l // 32) + v % 4 and c == l % 32
             seen.add((l, v))
     assert len(seen) == 1024
+
+
+def _fragment_read_addrs(compose, rows_base=0, kk=0):
+    """Byte addresses of one 128-bit MFMA fragment read: lane l reads row
+    (l & 31) at K-chunk 2·kk + (l >> 5) of a (rows × 64) fp16 LDS tile."""
+    M, B, S = compose
+    out = []
+    for l in range(64):
+        r = rows_base + (l & 31)
+        c = 2 * kk + (l >> 5)
+        out.append(2 * lay.compose_apply(M, B, S, "S[(256,64):(64@m,1@m)]", r * 64 + 8 * c))
+    return out
+
+
+@pytest.mark.parametrize("rows_base", [0, 32, 96])
+@pytest.mark.parametrize("kk", [0, 1, 3])
+def test_operand_swizzle_choice_under_bank_models(rows_base, kk):
+    """Why the kernels use ComposeLayout(3, 3, 4) rather than the pages'
+    128-byte mode (3, 3, 3): a 128-bit LDS read served 16 lanes per pass by 64
+    four-byte banks (the model gfx950's bank-conflict counter confirmed: 2-way
+    conflicts with (3,3,3), none with (3,3,4)) needs 16 consecutive rows on 16
+    distinct 16-byte slots of a 256-byte bank line.  Under the pages' own
+    32-bank, 8-lanes-per-pass model both are conflict-free."""
+    pages = _fragment_read_addrs((3, 3, 3), rows_base, kk)
+    pairs = _fragment_read_addrs((3, 3, 4), rows_base, kk)
+    assert lay.lds_access_cycles(pages, 16, 64, 4, 16) == 8   # 4 passes × 2-way
+    assert lay.lds_access_cycles(pairs, 16, 64, 4, 16) == 4   # 4 passes, no conflict
+    assert lay.lds_access_cycles(pages, 16, 32, 4, 8) == 8    # 8 passes, no conflict
+    # the direct-to-LDS copy writes 64 consecutive 16-byte slots per wave
+    # instruction: conflict-free whatever the swizzle
+    linear = [16 * l for l in range(64)]
+    assert lay.lds_access_cycles(linear, 16, 64, 4, 16) == 4
