@@ -53,7 +53,7 @@ constexpr int SWZ_ROW_SHIFT = 1;
 __host__ __device__ constexpr int swz(int r) { return (r >> SWZ_ROW_SHIFT) & 7; }
 __host__ __device__ constexpr int lds_chunk_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
 
-static_assert(tg::layout::check_swizzled_tile(tg::layout::swizzle_pairs_f16(256), 256, lds_chunk_off),
+static_assert(tg::layout::check_swizzled_tile(tg::layout::swizzle_pairs_f16(256), 256, 64, lds_chunk_off),
               "LDS chunk addressing disagrees with ComposeLayout(3, 3, 4)");
 
 // Fragment reads: lane l takes row (l & 31) and K-chunk (l >> 5) of a 32×16
@@ -74,7 +74,10 @@ static_assert(tg::layout::check_acc_fragment(acc_row_of, acc_col_of),
 // pages' persistent scheduler), so the workgroups resident on one XCD share
 // A and B bands in that XCD's L2.
 constexpr int NUM_XCD = 8;
-constexpr int GROUP_M = 8;
+#ifndef TG_GROUP_M
+#define TG_GROUP_M 4
+#endif
+constexpr int GROUP_M = TG_GROUP_M;
 
 __host__ __device__ constexpr void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
 {
@@ -321,16 +324,57 @@ __host__ __device__ constexpr bool dma_offsets_fit(int64_t rows, int64_t ld)
     return (rows - 1) * ld * 2 + 128 < (int64_t)DMA_RANGE;
 }
 
-__device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations (here: LDS
+// DMAs) are outstanding.  Inline assembly, so the compiler neither drops nor
+// relaxes it.
+template <int N>
+__device__ inline void wait_vmem()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt holds 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS reads (lgkmcnt), not
+// for its in-flight DMAs as __syncthreads would; the memory clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ inline void barrier_lds()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Operand tile in LDS: rows of BK_ fp16 (BK_/8 chunks of 16 bytes).  Chunk c
+// of row r sits at chunk c ^ swz(r), swz(r) = (r / ROWS_PER_LINE) mod RC, with
+// ROWS_PER_LINE the rows sharing one 256-byte bank line.  That is
+// ComposeLayout(per_element=3, swizzle_len=log2(RC), atom_len=4) over
+// S[(rows,BK_):(BK_@m,1@m)]: like the pages' 128-byte mode it keeps 16-byte
+// vectors whole and XORs row bits into the chunk index, but it takes the row
+// bits above the bank line, because gfx950's LDS has 64 four-byte banks and
+// serves a 128-bit read 16 lanes at a time — sixteen consecutive rows (the
+// first 16 lanes of an MFMA fragment read) then land on sixteen different
+// 16-byte bank slots.  (The 128-byte mode, for BK_ = 64, puts rows r and r+8
+// on the same banks: a measured 2-way conflict on every fragment read.)
+template <int BK_>
+struct OperandTile {
+    static constexpr int RC = BK_ / 8;
+    static constexpr int ROWS_PER_LINE = 128 / BK_;
+    static constexpr int ROWS_PER_DMA = 64 / RC;  // rows one wave DMA instruction fills
+    __host__ __device__ static constexpr int swz(int r) { return (r / ROWS_PER_LINE) & (RC - 1); }
+    __host__ __device__ static constexpr int off(int r, int c) { return r * BK_ + ((c ^ swz(r)) << 3); }
+};
+static_assert(tg::layout::check_swizzled_tile(tg::layout::swizzle_bank256_f16(256, 64), 256, 64,
+                                              OperandTile<64>::off),
+              "BK=64 LDS addressing disagrees with ComposeLayout(3, 3, 4)");
+static_assert(tg::layout::check_swizzled_tile(tg::layout::swizzle_bank256_f16(256, 32), 256, 32,
+                                              OperandTile<32>::off),
+              "BK=32 LDS addressing disagrees with ComposeLayout(3, 2, 4)");
 
 // Main path for 16-byte aligned operands with K, lda, ldb multiples of 8 and
 // in-tile byte offsets below 2^31 (see dma_offsets_fit).
 //
 // Operand tiles move global → LDS with buffer_load_dwordx4 … lds: one wave
-// instruction fills 64 consecutive 16-byte LDS slots, i.e. eight 128-byte
-// rows — exactly one atom of the 128-byte swizzle.  The swizzle is applied
-// on the source side: lane l fills physical chunk (l & 7) of row (l >> 3),
-// so it fetches logical chunk (l & 7) ^ (l >> 3) from global memory.
+// instruction fills 64 consecutive 16-byte LDS slots (ROWS_PER_DMA whole
+// rows), so the swizzle is applied on the source side: lane l fills physical
+// chunk l mod RC of row l / RC and fetches the logical chunk stored there.
 // Each DMA is a buffer descriptor whose base is the tile origin + k (in
 // SGPRs) plus a per-lane 32-bit offset fixed for the whole K loop.  (The
 // buffer form, unlike the global form, lets the compiler keep partial
@@ -339,32 +383,47 @@ __device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "
 // Tails: rows of A past M only feed rows of D past M, which are never
 // stored (likewise B and N), so such rows are clamped to the last valid row
 // instead of being zeroed.  Past K both operands must be exactly zero
-// (0·NaN would poison valid outputs): in the last K-tile, when K % 64 != 0,
-// lanes whose chunk lies beyond K get an offset past the descriptor's range,
-// for which the buffer unit returns zeros.
+// (0·NaN would poison valid outputs): in the last K-tile, lanes whose chunk
+// lies beyond K get an offset past the descriptor's range, for which the
+// buffer unit returns zeros.
 //
-// K loop (two LDS stages, fragments double-buffered in registers):
-//   stage s holds K-tile kt; the DMA for K-tile kt+1 is in flight into s^1;
-//   K-steps 0..2: read the next K-step's fragments, then issue this step's MFMAs;
-//   wait for this wave's DMA, barrier (stage s^1 complete, stage s drained);
-//   read K-step 0 of stage s^1, issue K-step 3's MFMAs from registers, and
-//   start the DMA of K-tile kt+2 into stage s.
-template <int BM, int BN, int WM, int WN>
+// K loop over STAGES LDS stages (a ring, as in the pages' multi-stage
+// pipeline, with waits and barriers in place of mbarrier phases):
+//   stage kt mod STAGES holds K-tile kt; DMAs for K-tiles kt+1 .. kt+STAGES-1
+//   are in flight (the prologue issues K-tiles 0 .. STAGES-1);
+//   K-steps 0 .. KSTEPS-2 each read the next step's fragments into the other
+//   register buffer while issuing their own MFMAs;
+//   wait until K-tile kt+1 has landed (vmcnt), barrier: every wave has
+//   finished reading stage kt mod STAGES;
+//   the last K-step's MFMAs run from registers while the next stage's K-step
+//   0 is read and the drained stage is refilled with K-tile kt+STAGES (past
+//   the end: an all-out-of-range DMA, i.e. a no-op that keeps the loop
+//   branch-free and the vmcnt bookkeeping uniform).
+template <int BM, int BN, int WM, int WN, int BK_, int STAGES>
 __global__ __launch_bounds__(WM *WN * 64) TG_ONE_WAVE_PER_SIMD void gemm_f16_dma_kernel(
     const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
     int dvec)
 {
+    using T = OperandTile<BK_>;
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int A_PASSES = BM / 8 / NW, B_PASSES = BN / 8 / NW;
+    constexpr int KSTEPS = BK_ / 16;
+    constexpr int A_PASSES = BM / T::ROWS_PER_DMA / NW, B_PASSES = BN / T::ROWS_PER_DMA / NW;
+    constexpr int DMA_PER_TILE = A_PASSES + B_PASSES;
+    constexpr int STAGE = (BM + BN) * BK_;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "row groups must split over waves");
-    constexpr int STAGE = (BM + BN) * BK;
-    static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS budget");
+    static_assert((BM / T::ROWS_PER_DMA) % NW == 0 && (BN / T::ROWS_PER_DMA) % NW == 0,
+                  "DMA row groups must split evenly over the waves");
+    static_assert(KSTEPS % 2 == 0, "fragment buffers alternate per K-step");
+    static_assert(STAGES >= 2 && STAGES * STAGE * 2 <= 160 * 1024, "LDS budget");
+    // At the wait of iteration kt, K-tiles up to kt+STAGES-1 have been issued;
+    // K-tile kt+1 must have landed, so STAGES-2 K-tiles may stay in flight.
+    constexpr int VM_IN_FLIGHT = (STAGES - 2) * DMA_PER_TILE;
+    static_assert((STAGES - 1) * DMA_PER_TILE <= 63, "vmcnt holds 6 bits");
 
-    __shared__ __attribute__((aligned(1024))) _Float16 smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) _Float16 smem[STAGES * STAGE];
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -374,63 +433,68 @@ __global__ __launch_bounds__(WM *WN * 64) TG_ONE_WAVE_PER_SIMD void gemm_f16_dma
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    // DMA source of this lane in pass p: tile row t = 8·(p·NW + wave) + (lane >> 3),
-    // whose physical chunk (lane & 7) holds logical chunk (lane & 7) ^ swz(t);
-    // byte offsets from the tile origin.  kc[p] is the logical chunk (for the
-    // K-tail test).
-    const int dr = lane >> 3;
+    // DMA source of this lane in pass p: tile row t = ROWS_PER_DMA·(p·NW + wave)
+    // + lane / RC, whose physical chunk lane mod RC holds logical chunk
+    // kc = (lane mod RC) ^ swz(t); byte offset from the tile origin.
+    const int dr = lane / T::RC, dpc = lane % T::RC;
     uint32_t a_off[A_PASSES], b_off[B_PASSES];
     int a_kc[A_PASSES], b_kc[B_PASSES];
 #pragma unroll
     for (int p = 0; p < A_PASSES; ++p) {
-        const int t = 8 * (p * NW + wave) + dr;
-        a_kc[p] = (lane & 7) ^ swz(t);
-        const int r = imin(t, M - 1 - m0);
-        a_off[p] = (uint32_t)(r * lda * 2 + 16 * a_kc[p]);
+        const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
+        a_kc[p] = dpc ^ T::swz(t);
+        a_off[p] = (uint32_t)(imin(t, M - 1 - m0) * lda * 2 + 16 * a_kc[p]);
     }
 #pragma unroll
     for (int p = 0; p < B_PASSES; ++p) {
-        const int t = 8 * (p * NW + wave) + dr;
-        b_kc[p] = (lane & 7) ^ swz(t);
-        const int r = imin(t, N - 1 - n0);
-        b_off[p] = (uint32_t)(r * ldb * 2 + 16 * b_kc[p]);
+        const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
+        b_kc[p] = dpc ^ T::swz(t);
+        b_off[p] = (uint32_t)(imin(t, N - 1 - n0) * ldb * 2 + 16 * b_kc[p]);
     }
     const char *a_tile = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
     const char *b_tile = reinterpret_cast<const char *>(B + (int64_t)n0 * ldb);
+    const int KT = (K + BK_ - 1) / BK_;
 
-    // DMA of K-tile kt into stage s.  Chunks past K read out of range (zeros;
-    // only the last K-tile has any); kt >= KT makes every lane out of range,
-    // a no-op copy of zeros that keeps the caller's loop free of branches.
-    auto dma = [&](int kt, int s) {
-        const int k = kt * BK;
-        const int klim = kt < (K + BK - 1) / BK ? K - k : 0;  // valid K in this tile
-        _Float16 *as = smem + s * STAGE;
-        _Float16 *bs = as + BM * BK;
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a_tile + 2 * k), (short)0, DMA_RANGE, BUFFER_RSRC_WORD3);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(b_tile + 2 * k), (short)0, DMA_RANGE, BUFFER_RSRC_WORD3);
-#pragma unroll
-        for (int p = 0; p < A_PASSES; ++p)
-            dma16(ra, as + (p * NW + wave) * 8 * BK, 8 * a_kc[p] < klim ? a_off[p] : DMA_OOB);
-#pragma unroll
-        for (int p = 0; p < B_PASSES; ++p)
-            dma16(rb, bs + (p * NW + wave) * 8 * BK, 8 * b_kc[p] < klim ? b_off[p] : DMA_OOB);
+    struct DmaTile {
+        __amdgpu_buffer_rsrc_t ra, rb;
+        _Float16 *as, *bs;
+        int klim;  // valid K elements in this K-tile (0 past the end)
+    };
+    auto dma_tile = [&](int kt) {
+        const int k = kt * BK_;
+        DmaTile d;
+        d.ra = __builtin_amdgcn_make_buffer_rsrc((void *)(a_tile + 2 * k), (short)0, DMA_RANGE,
+                                                 BUFFER_RSRC_WORD3);
+        d.rb = __builtin_amdgcn_make_buffer_rsrc((void *)(b_tile + 2 * k), (short)0, DMA_RANGE,
+                                                 BUFFER_RSRC_WORD3);
+        d.as = smem + (kt % STAGES) * STAGE;
+        d.bs = d.as + BM * BK_;
+        d.klim = kt < KT ? K - k : 0;
+        return d;
+    };
+    // i-th DMA of a K-tile: A passes first, then B passes
+    auto dma_pass = [&](const DmaTile &d, int i) {
+        if (i < A_PASSES)
+            dma16(d.ra, d.as + (i * NW + wave) * T::ROWS_PER_DMA * BK_,
+                  8 * a_kc[i] < d.klim ? a_off[i] : DMA_OOB);
+        else
+            dma16(d.rb, d.bs + ((i - A_PASSES) * NW + wave) * T::ROWS_PER_DMA * BK_,
+                  8 * b_kc[i - A_PASSES] < d.klim ? b_off[i - A_PASSES] : DMA_OOB);
     };
 
     const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
     f16x8 fa[2][TM], fb[2][TN];
-
-    // one fragment: q < TM is A fragment q, else B fragment q - TM
+    // one fragment of K-step kk of the K-tile in stage s: q < TM is A
+    // fragment q, else B fragment q - TM
     auto read_frag = [&](int s, int kk, int q, f16x8 *a, f16x8 *b) {
         const _Float16 *as = smem + s * STAGE;
-        const _Float16 *bs = as + BM * BK;
+        const _Float16 *bs = as + BM * BK_;
         const int c = kk * 2 + frag_hi;
         if (q < TM)
-            a[q] = *reinterpret_cast<const f16x8 *>(as + lds_chunk_off(wm * WTM + q * 32 + frag_row, c));
+            a[q] = *reinterpret_cast<const f16x8 *>(as + T::off(wm * WTM + q * 32 + frag_row, c));
         else
             b[q - TM] = *reinterpret_cast<const f16x8 *>(
-                bs + lds_chunk_off(wn * WTN + (q - TM) * 32 + frag_row, c));
+                bs + T::off(wn * WTN + (q - TM) * 32 + frag_row, c));
     };
 
     f32x16 acc[TM][TN];
@@ -446,130 +510,121 @@ __global__ __launch_bounds__(WM *WN * 64) TG_ONE_WAVE_PER_SIMD void gemm_f16_dma
     // pinned between them in program order (sched_barrier fences each slot):
     // after MFMA i comes the next K-step's LDS read i (for i < TM+TN, in the
     // order the next step first uses them: A0, B0..B(TN-1), A1..A(TM-1)) and,
-    // when `with_dma`, DMA pass i.  The matrix core runs each MFMA while the
-    // wave issues the companions; fewer than 16 LDS reads are ever in flight,
-    // so the compiler's waits stay partial.
+    // when `dma` is given, DMA pass i.  The matrix core runs each MFMA while
+    // the wave issues the companions; fewer than 16 LDS reads are ever in
+    // flight, so the compiler's lgkmcnt waits stay partial.
     constexpr int NFRAG = TM + TN;
-    // read slot i → fragment id (q < TM: A fragment q, else B fragment q - TM)
+    constexpr int SLOTS = TM * TN;
     auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
-    auto step = [&](const f16x8 *a, const f16x8 *b, int rs, int rkk, f16x8 *na, f16x8 *nb,
-                    bool with_reads, bool with_dma, int dkt, int ds) {
-        const int k = dkt * BK;
-        const int klim = dkt < (K + BK - 1) / BK ? K - k : 0;  // valid K in that K-tile
-        _Float16 *das = smem + ds * STAGE;
-        _Float16 *dbs = das + BM * BK;
-        __amdgpu_buffer_rsrc_t ra, rb;
-        if (with_dma) {
-            ra = __builtin_amdgcn_make_buffer_rsrc((void *)(a_tile + 2 * k), (short)0, DMA_RANGE,
-                                                   BUFFER_RSRC_WORD3);
-            rb = __builtin_amdgcn_make_buffer_rsrc((void *)(b_tile + 2 * k), (short)0, DMA_RANGE,
-                                                   BUFFER_RSRC_WORD3);
-        }
+    auto step = [&](const f16x8 *a, const f16x8 *b, bool with_reads, int rs, int rkk, f16x8 *na,
+                    f16x8 *nb, const DmaTile *dma) {
 #pragma unroll
-        for (int i = 0; i < TM * TN; ++i) {
+        for (int i = 0; i < SLOTS; ++i) {
             const int ti = i / TN, tj = i % TN;
             acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[tj], a[ti], acc[ti][tj], 0, 0, 0);
             if (with_reads && i < NFRAG)
                 read_frag(rs, rkk, frag_of_slot(i), na, nb);
-            if (with_dma && i < A_PASSES)
-                dma16(ra, das + (i * NW + wave) * 8 * BK, 8 * a_kc[i] < klim ? a_off[i] : DMA_OOB);
-            if (with_dma && i >= A_PASSES && i < A_PASSES + B_PASSES) {
-                const int p = i - A_PASSES;
-                dma16(rb, dbs + (p * NW + wave) * 8 * BK, 8 * b_kc[p] < klim ? b_off[p] : DMA_OOB);
-            }
+            if (dma && i < DMA_PER_TILE)
+                dma_pass(*dma, i);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // any reads left over when there are more fragments than MFMA slots
 #pragma unroll
-        for (int i = TM * TN; i < NFRAG; ++i)
+        for (int i = SLOTS; i < NFRAG; ++i)  // reads left when fragments outnumber slots
             if (with_reads)
                 read_frag(rs, rkk, frag_of_slot(i), na, nb);
+#pragma unroll
+        for (int i = SLOTS; i < DMA_PER_TILE; ++i)  // likewise DMA passes
+            if (dma)
+                dma_pass(*dma, i);
     };
 
-    // DMA of K-tile kt into stage s, passes `from` onwards, outside the MFMA
-    // stream (prologue, and shapes whose passes outnumber the MFMA slots).
-    // Chunks past K read out of range, i.e. zeros; only the last K-tile has
-    // any.  kt >= KT makes every lane out of range: a no-op copy of zeros.
-    auto dma_rest = [&](int kt, int s, int from) {
-        const int k = kt * BK;
-        const int klim = kt < (K + BK - 1) / BK ? K - k : 0;
-        _Float16 *as = smem + s * STAGE;
-        _Float16 *bs = as + BM * BK;
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a_tile + 2 * k), (short)0, DMA_RANGE, BUFFER_RSRC_WORD3);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(b_tile + 2 * k), (short)0, DMA_RANGE, BUFFER_RSRC_WORD3);
+    // prologue: K-tiles 0 .. STAGES-1 fill every stage (iteration kt refills
+    // stage kt mod STAGES with K-tile kt+STAGES); wait for K-tile 0
 #pragma unroll
-        for (int p = 0; p < A_PASSES; ++p)
-            if (p >= from)
-                dma16(ra, as + (p * NW + wave) * 8 * BK, 8 * a_kc[p] < klim ? a_off[p] : DMA_OOB);
+    for (int t = 0; t < STAGES; ++t) {
+        const DmaTile d = dma_tile(t);
 #pragma unroll
-        for (int p = 0; p < B_PASSES; ++p)
-            if (A_PASSES + p >= from)
-                dma16(rb, bs + (p * NW + wave) * 8 * BK, 8 * b_kc[p] < klim ? b_off[p] : DMA_OOB);
-    };
-    constexpr int DMA_IN_STREAM = (A_PASSES + B_PASSES) < TM * TN ? (A_PASSES + B_PASSES) : TM * TN;
-
-    const int KT = (K + BK - 1) / BK;
-    if (KT > 0) {
-        dma_rest(0, 0, 0);
-        wait_vmem_all();
-        __syncthreads();
-        dma_rest(1, 1, 0);  // a no-op when KT == 1
-#pragma unroll
-        for (int q = 0; q < NFRAG; ++q)
-            read_frag(0, 0, q, fa[0], fb[0]);
+        for (int i = 0; i < DMA_PER_TILE; ++i)
+            dma_pass(d, i);
     }
-    // K-steps 0..2 of the K-tile in stage s, each with the next step's reads.
-    auto first_three_steps = [&](int s) {
+    wait_vmem<(STAGES - 1) * DMA_PER_TILE>();
+    barrier_lds();
 #pragma unroll
-        for (int kk = 0; kk < BK / 16 - 1; ++kk)
-            step(fa[kk & 1], fb[kk & 1], s, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], true,
-                 false, 0, 0);
+    for (int q = 0; q < NFRAG; ++q)
+        read_frag(0, 0, q, fa[0], fb[0]);
+
+    // K-steps 0 .. KSTEPS-2 of the K-tile in stage s, each reading the next
+    // step's fragments; the last step's fragments end up in buffer 1
+    auto leading_steps = [&](int s) {
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS - 1; ++kk)
+            step(fa[kk & 1], fb[kk & 1], true, s, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1],
+                 nullptr);
     };
-    // steady state: a next K-tile exists (peeled so the loop body is straight-line)
+    // steady state: a next K-tile exists (the last one is peeled off so the
+    // loop body is straight-line)
     for (int kt = 0; kt < KT - 1; ++kt) {
-        const int s = kt & 1;
-        first_three_steps(s);
-        wait_vmem_all();
-        __syncthreads();
-        // stage s is drained: K-step 3 runs from registers while the next
-        // stage's K-step 0 is read and stage s is refilled with K-tile kt+2
-        // (a no-op copy of zeros past the end)
-        step(fa[1], fb[1], s ^ 1, 0, fa[0], fb[0], true, true, kt + 2, s);
-        if (DMA_IN_STREAM < A_PASSES + B_PASSES)
-            dma_rest(kt + 2, s, DMA_IN_STREAM);
+        const int s = kt % STAGES;
+        leading_steps(s);
+        wait_vmem<VM_IN_FLIGHT>();  // K-tile kt+1 has landed (this wave's part)
+        barrier_lds();              // ... for every wave; stage s is drained
+        const DmaTile d = dma_tile(kt + STAGES);
+        step(fa[1], fb[1], true, (kt + 1) % STAGES, 0, fa[0], fb[0], &d);
     }
     if (KT > 0) {
-        first_three_steps((KT - 1) & 1);
-        step(fa[1], fb[1], 0, 0, fa[0], fb[0], false, false, 0, 0);
+        leading_steps((KT - 1) % STAGES);
+        step(fa[1], fb[1], false, 0, 0, fa[0], fb[0], nullptr);
     }
-    wait_vmem_all();  // no LDS DMA may be outstanding when the wave ends
+    wait_vmem<0>();  // no LDS DMA may be outstanding when the wave ends
 
-    // Epilogue (same register → D map as the element-wise path).
+    // Epilogue, staged through LDS so that global stores are whole lines.
+    // Accumulator register v of lane l holds D row (l % 32) and D column
+    // 8·(v/4) + 4·(l/32) + v%4 of its 32×32 tile.  After a barrier (every wave
+    // is done with the operand stages) each wave writes its WTM×WTN block as
+    // fp16 into its own region of the stage memory — row-major, 16-byte chunk
+    // index XORed with the row so the 32 rows one write instruction touches
+    // spread over the banks — then reads it back 16 bytes per lane along rows
+    // and stores those: each store instruction writes 64·16 bytes as
+    // contiguous row segments.  Conversion is fp32 → fp16 round-to-nearest-even.
+    static_assert(NW * WTM * WTN * 2 <= STAGES * STAGE * 2, "staging fits in the stage memory");
+    constexpr int SROW = WTN;                 // staging row length (elements)
+    constexpr int SCH = WTN / 8;              // 16-byte chunks per staging row
+    static_assert((SCH & (SCH - 1)) == 0 && SCH >= 2, "chunk swizzle needs a power of two");
+    auto stage_off = [](int r, int chunk) { return r * SROW + ((chunk ^ (r & (SCH - 1))) << 3); };
+    barrier_lds();
+    _Float16 *stg = smem + wave * WTM * WTN;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int row = m0 + wm * WTM + i * 32 + frag_row;
-        if (row >= M)
-            continue;
-        _Float16 *drow = D + (int64_t)row * ldd;
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * WTN + j * 32 + g * 8 + frag_hi * 4;
                 f16x4 h;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[r] = (_Float16)acc[i][j][g * 4 + r];
-                if (dvec && col + 3 < N) {
-                    *reinterpret_cast<f16x4 *>(drow + col) = h;
-                } else {
+                    h[r] = (_Float16)acc[i][j][g * 4 + r];  // round to nearest even
+                const int r = i * 32 + frag_row;
+                const int c = j * 32 + g * 8 + frag_hi * 4;
+                *reinterpret_cast<f16x4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
+            }
+    // read back: lane l takes chunk l mod SCH of row l / SCH (+ 64/SCH rows per pass)
+    constexpr int ROWS_PER_PASS = 64 / SCH;
+    const int rc = lane % SCH, rr = lane / SCH;
+    const int col = n0 + wn * WTN + 8 * rc;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (col + r < N)
-                            drow[col + r] = h[r];
-                }
+    for (int pass = 0; pass < WTM / ROWS_PER_PASS; ++pass) {
+        const int r = pass * ROWS_PER_PASS + rr;
+        const f16x8 v = *reinterpret_cast<const f16x8 *>(stg + stage_off(r, rc));
+        const int row = m0 + wm * WTM + r;
+        if (row < M) {
+            _Float16 *dst = D + (int64_t)row * ldd + col;
+            if (dvec && col + 7 < N) {
+                *reinterpret_cast<f16x8 *>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < N)
+                        dst[e] = v[e];
             }
         }
     }
@@ -579,21 +634,44 @@ struct KernelChoice {
     const void *fn;
     const char *name;
     int bm, bn, threads;
+    int path;
 };
+
+// Compile-time tuning of the direct-to-LDS kernels: K-tile depth (BK) and
+// LDS ring depth (STAGES) per workgroup tile size (L: 256×256, M: 128×128,
+// S: 64×64).  The defaults are the measured best on MI355X.
+#ifndef TG_L_BK
+#define TG_L_BK 64
+#endif
+#ifndef TG_L_STAGES
+#define TG_L_STAGES 2
+#endif
+#ifndef TG_M_BK
+#define TG_M_BK 64
+#endif
+#ifndef TG_M_STAGES
+#define TG_M_STAGES 2
+#endif
+#ifndef TG_S_BK
+#define TG_S_BK 32
+#endif
+#ifndef TG_S_STAGES
+#define TG_S_STAGES 4
+#endif
 
 // Load path of a launch: direct-to-LDS DMA, 16-byte loads through registers
 // (aligned operands whose in-tile offsets exceed 32 bits), or element-wise.
 enum LoadPath { PATH_DMA = 0, PATH_VEC = 1, PATH_SCALAR = 2 };
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int DMA_BK, int DMA_STAGES>
 KernelChoice choice(LoadPath path, const char *const names[3])
 {
     const void *fn = path == PATH_DMA
-                         ? reinterpret_cast<const void *>(&gemm_f16_dma_kernel<BM, BN, WM, WN>)
+                         ? reinterpret_cast<const void *>(&gemm_f16_dma_kernel<BM, BN, WM, WN, DMA_BK, DMA_STAGES>)
                      : path == PATH_VEC
                          ? reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, true>)
                          : reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, false>);
-    return {fn, names[path], BM, BN, WM * WN * 64};
+    return {fn, names[path], BM, BN, WM * WN * 64, path};
 }
 
 constexpr const char *NAMES_256[3] = {"gemm_f16_256x256_w2x2_dma", "gemm_f16_256x256_w2x2_vec",
@@ -639,16 +717,18 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     };
     KernelChoice k;
     if (tiles(256, 256) >= NUM_CU)
-        k = choice<256, 256, 2, 2>(path(256, 256), NAMES_256);
+        k = choice<256, 256, 2, 2, TG_L_BK, TG_L_STAGES>(path(256, 256), NAMES_256);
     else if (tiles(128, 128) >= NUM_CU)
-        k = choice<128, 128, 2, 2>(path(128, 128), NAMES_128);
+        k = choice<128, 128, 2, 2, TG_M_BK, TG_M_STAGES>(path(128, 128), NAMES_128);
     else
-        k = choice<64, 64, 2, 2>(path(64, 64), NAMES_64);
+        k = choice<64, 64, 2, 2, TG_S_BK, TG_S_STAGES>(path(64, 64), NAMES_64);
     Plan p;
     p.k = k;
     p.tiles_m = (int)((M + k.bm - 1) / k.bm);
     p.tiles_n = (int)((N + k.bn - 1) / k.bn);
-    p.dvec = (ldd % 4 == 0) && ((uintptr_t)D % 8 == 0);
+    // vector stores: 16 bytes (staged epilogue of the DMA kernels) or 8 bytes
+    p.dvec = p.k.path == PATH_DMA ? (ldd % 8 == 0) && ((uintptr_t)D % 16 == 0)
+                                  : (ldd % 4 == 0) && ((uintptr_t)D % 8 == 0);
     return p;
 }
 

@@ -222,6 +222,15 @@ constexpr ComposeLayout swizzle128_f16(int64_t rows)
     return ComposeLayout{Swizzle{3, 3, 3, true}, row_major(rows, 64)};
 }
 
+// Operand-tile swizzle for a (rows × cols) fp16 tile, cols in {16, 32, 64}:
+// ComposeLayout(3, log2(cols/8), 4) — 16-byte vectors stay whole and the
+// chunk index is XORed with the row bits above one 256-byte line.
+constexpr int ilog2(int64_t x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+constexpr ComposeLayout swizzle_bank256_f16(int64_t rows, int64_t cols)
+{
+    return ComposeLayout{Swizzle{3, ilog2(cols / 8), 4, true}, row_major(rows, cols)};
+}
+
 // The operand-tile swizzle the kernels use: ComposeLayout(3, 3, 4) over
 // S[(rows,64):(64@m,1@m)], i.e. 16-byte chunk c of row r lands at chunk
 // c ^ ((r >> 1) & 7).  Same vector-keeping M = 3 as the 128-byte mode, but the
@@ -270,14 +279,14 @@ constexpr TileLayout mfma32x32_acc_swapped()
 // The kernels' LDS chunk address fn(r, c) (element offset of 16-byte chunk c
 // of row r) equals layout L for every element of a (rows × 64) tile.
 template <class F>
-constexpr bool check_swizzled_tile(const ComposeLayout &L, int rows, F fn)
+constexpr bool check_swizzled_tile(const ComposeLayout &L, int rows, int cols, F fn)
 {
     if (!L.well_formed())
         return false;
     for (int r = 0; r < rows; ++r)
-        for (int c = 0; c < 8; ++c)
+        for (int c = 0; c < cols / 8; ++c)
             for (int e = 0; e < 8; ++e)
-                if (fn(r, c) + e != L.apply2(r, c * 8 + e, 64))
+                if (fn(r, c) + e != L.apply2(r, c * 8 + e, cols))
                     return false;
     return true;
 }
