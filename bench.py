@@ -50,6 +50,73 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
+def _pmc_per_dispatch(csv_path: str, counter: str, name_part: str):
+    """Mean value of `counter` over the dispatches whose kernel name contains
+    `name_part` in a rocprofv3 --pmc counter_collection.csv."""
+    import csv
+    import collections
+
+    per = collections.defaultdict(float)
+    for row in csv.DictReader(open(csv_path)):
+        if row["Counter_Name"] == counter and name_part in row["Kernel_Name"]:
+            per[row["Dispatch_Id"]] += float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernels matching {name_part!r} in {csv_path}")
+    vals = list(per.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_record(args) -> int:
+    """Turn four rocprofv3 --pmc runs (GEMM FETCH_SIZE, GEMM WRITE_SIZE, copy
+    FETCH_SIZE, copy WRITE_SIZE) into profiles/<kernel>__<workload>__traffic.json.
+    Each GEMM counter is scaled by (known copy bytes / the same counter for
+    the copy kernel)."""
+    gf, gw, cf, cw = args.traffic_record
+    copy_bytes = args.copy_bytes
+    kernel, workload = args.traffic_kernel, args.workload
+    g_fetch, n1 = _pmc_per_dispatch(gf, "FETCH_SIZE", "gemm_f16")
+    g_write, n2 = _pmc_per_dispatch(gw, "WRITE_SIZE", "gemm_f16")
+    c_fetch, _ = _pmc_per_dispatch(cf, "FETCH_SIZE", "copyBuffer")
+    c_write, _ = _pmc_per_dispatch(cw, "WRITE_SIZE", "copyBuffer")
+    k_fetch = copy_bytes / c_fetch  # bytes per counter unit (nominally 1024: KiB)
+    k_write = copy_bytes / c_write
+    rec = {
+        "kernel": kernel,
+        "workload": workload,
+        "kernel_source_sha256": kernel_source_digest(),
+        "fetch_counter_per_dispatch": g_fetch,
+        "write_counter_per_dispatch": g_write,
+        "dispatches": [n1, n2],
+        "copy_bytes": copy_bytes,
+        "copy_fetch_counter": c_fetch,
+        "copy_write_counter": c_write,
+        "bytes_per_fetch_unit": k_fetch,
+        "bytes_per_write_unit": k_write,
+        "hbm_read_bytes_per_launch": g_fetch * k_fetch,
+        "hbm_write_bytes_per_launch": g_write * k_write,
+        "hbm_bytes_per_launch": g_fetch * k_fetch + g_write * k_write,
+    }
+    path = os.path.join(PROFILES, f"{kernel}__{workload}__traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+    return 0
+
+
+def copy_only(nbytes: int, reps: int = 5) -> int:
+    """A plain device-to-device copy of `nbytes` (the calibration kernel)."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {nbytes} bytes x {reps}", file=sys.stderr)
+    return 0
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary for
     this kernel and workload, or None when there is none or the kernel
@@ -147,13 +214,25 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="linear_8192x14336x4096")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target length of the oracle sample")
     ap.add_argument("--cpu-rows", type=int, default=None, help="fixed oracle sample size in rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and print a table on stderr")
+    ap.add_argument("--copy-bytes", type=int, default=None,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--traffic-record", nargs=4, metavar="CSV", default=None,
+                    help="GEMM FETCH_SIZE, GEMM WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE "
+                         "counter_collection.csv files -> profiles/*__traffic.json")
+    ap.add_argument("--traffic-kernel", default=None, help="kernel name for --traffic-record")
     args = ap.parse_args()
+
+    if args.traffic_record:
+        if not args.copy_bytes or not args.traffic_kernel:
+            print("--traffic-record needs --copy-bytes and --traffic-kernel", file=sys.stderr)
+            return 2
+        return traffic_record(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -165,6 +244,8 @@ def main() -> int:
 
     import workloads
 
+    if args.copy_bytes and not args.traffic_record:
+        return copy_only(args.copy_bytes)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
