@@ -399,7 +399,7 @@ static_assert(tg::layout::check_swizzled_tile(tg::layout::swizzle_bank256_f16(25
 //   0 is read and the drained stage is refilled with K-tile kt+STAGES (past
 //   the end: an all-out-of-range DMA, i.e. a no-op that keeps the loop
 //   branch-free and the vmcnt bookkeeping uniform).
-template <int BM, int BN, int WM, int WN, int BK_, int STAGES, int OCC, int DMA_STEPS>
+template <int BM, int BN, int WM, int WN, int BK_, int STAGES, int OCC, int DMA_STEPS, int KROT>
 __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC) void gemm_f16_dma_kernel(
     const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
@@ -460,8 +460,19 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC) void gemm_f16_d
         _Float16 *as, *bs;
         int klim;  // valid K elements in this K-tile (0 past the end)
     };
+    // K-tile order: this workgroup starts at K-tile krot and wraps around.
+    // With KROT the eight XCDs (workgroup w runs on XCD w mod 8) start at
+    // K offsets spread evenly over the row, so that at any moment the XCDs
+    // stream from different address ranges of B instead of all requesting
+    // the same column band of every row; a streaming (HBM-bound) launch
+    // gains about a quarter of its bandwidth.  Only the order of the K
+    // summation changes.
+    const int krot = KROT && KT > 0 ? (int)(blockIdx.x % 8) * KT / 8 : 0;
     auto dma_tile = [&](int kt) {
-        const int k = kt * BK_;
+        int pk = kt + krot;
+        if (pk >= KT)
+            pk -= KT;
+        const int k = pk * BK_;
         DmaTile d;
         d.ra = __builtin_amdgcn_make_buffer_rsrc((void *)(a_tile + 2 * k), (short)0, DMA_RANGE,
                                                  BUFFER_RSRC_WORD3);
@@ -923,18 +934,24 @@ struct KernelChoice {
 #ifndef TG_S_STAGES
 #define TG_S_STAGES 4
 #endif
+#ifndef TG_S_KROT
+#define TG_S_KROT 0
+#endif
+#ifndef TG_M_KROT
+#define TG_M_KROT 0
+#endif
 
 // Load path of a launch: direct-to-LDS DMA, 16-byte loads through registers
 // (aligned operands whose in-tile offsets exceed 32 bits), or element-wise.
 enum LoadPath { PATH_DMA = 0, PATH_VEC = 1, PATH_SCALAR = 2 };
 
 template <int BM, int BN, int WM, int WN, int DMA_BK, int DMA_STAGES, int DMA_STEPS = 1,
-          int OCC = 1>
+          int OCC = 1, int KROT = 0>
 KernelChoice choice(LoadPath path, const char *const names[3])
 {
     const void *fn = path == PATH_DMA
                          ? reinterpret_cast<const void *>(
-                               &gemm_f16_dma_kernel<BM, BN, WM, WN, DMA_BK, DMA_STAGES, OCC, DMA_STEPS>)
+                               &gemm_f16_dma_kernel<BM, BN, WM, WN, DMA_BK, DMA_STAGES, OCC, DMA_STEPS, KROT>)
                      : path == PATH_VEC
                          ? reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, true>)
                          : reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, false>);
@@ -943,9 +960,55 @@ KernelChoice choice(LoadPath path, const char *const names[3])
 
 constexpr const char *NAMES_256[3] = {"gemm_f16_256x256_w2x2_dma", "gemm_f16_256x256_w2x2_vec",
                                       "gemm_f16_256x256_w2x2_scalar"};
-constexpr const char *NAMES_256x128[3] = {"gemm_f16_256x128_w2x2_dma",
+[[maybe_unused]] constexpr const char *NAMES_256x128[3] = {"gemm_f16_256x128_w2x2_dma",
                                           "gemm_f16_256x128_w2x2_vec",
                                           "gemm_f16_256x128_w2x2_scalar"};
+#define TG_STR2(x) #x
+#define TG_STR(x) TG_STR2(x)
+#define TG_NAMES(bm, bn, wm, wn)                                                              \
+    {"gemm_f16_" TG_STR(bm) "x" TG_STR(bn) "_w" TG_STR(wm) "x" TG_STR(wn) "_dma",             \
+     "gemm_f16_" TG_STR(bm) "x" TG_STR(bn) "_w" TG_STR(wm) "x" TG_STR(wn) "_vec",             \
+     "gemm_f16_" TG_STR(bm) "x" TG_STR(bn) "_w" TG_STR(wm) "x" TG_STR(wn) "_scalar"}
+// Column-strip tiles for small M: one tile row covers all of M.
+#ifndef TG_K_BN
+#define TG_K_BN 128
+#endif
+#ifndef TG_K_WN
+#define TG_K_WN 4
+#endif
+#ifndef TG_K_STAGES
+#define TG_K_STAGES 4
+#endif
+#ifndef TG_K_BK
+#define TG_K_BK 64
+#endif
+#ifndef TG_K_DS
+#define TG_K_DS 2
+#endif
+#ifndef TG_K_ON
+#define TG_K_ON 1
+#endif
+#ifndef TG_K2_WM
+#define TG_K2_WM 2
+#endif
+#ifndef TG_K2_STAGES
+#define TG_K2_STAGES 4
+#endif
+#ifndef TG_K2_BK
+#define TG_K2_BK 64
+#endif
+#ifndef TG_K4_STAGES
+#define TG_K4_STAGES 3
+#endif
+#ifndef TG_K4_BK
+#define TG_K4_BK 64
+#endif
+#ifndef TG_K_MAXM
+#define TG_K_MAXM 256
+#endif
+constexpr const char *NAMES_STRIP64[3] = TG_NAMES(64, TG_K_BN, 1, TG_K_WN);
+constexpr const char *NAMES_STRIP128[3] = TG_NAMES(128, 128, TG_K2_WM, 4 / TG_K2_WM);
+constexpr const char *NAMES_STRIP256[3] = TG_NAMES(256, 128, 2, 2);
 constexpr const char *NAMES_128[3] = {"gemm_f16_128x128_w2x2_dma", "gemm_f16_128x128_w2x2_vec",
                                       "gemm_f16_128x128_w2x2_scalar"};
 constexpr const char *NAMES_64[3] = {"gemm_f16_64x64_w2x2_dma", "gemm_f16_64x64_w2x2_vec",
@@ -986,6 +1049,17 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
         return dma_offsets_fit(bm, lda) && dma_offsets_fit(bn, ldb) ? PATH_DMA : PATH_VEC;
     };
     KernelChoice k;
+    // Small M, large N (HBM-bound streaming of B): one tile row covers all of
+    // M, so B is read exactly once, and the XCDs start at spread K offsets.
+    if (TG_K_ON && M <= 64 && tiles(64, TG_K_BN) >= NUM_CU / 2)
+        k = choice<64, TG_K_BN, 1, TG_K_WN, TG_K_BK, TG_K_STAGES, TG_K_DS, 1, 1>(path(64, TG_K_BN),
+                                                                                  NAMES_STRIP64);
+    else if (TG_K_ON && M <= 128 && TG_K_MAXM >= 128 && tiles(128, 128) >= NUM_CU / 2)
+        k = choice<128, 128, TG_K2_WM, 4 / TG_K2_WM, TG_K2_BK, TG_K2_STAGES, 2, 1, 1>(path(128, 128),
+                                                                                       NAMES_STRIP128);
+    else if (TG_K_ON && M <= 256 && TG_K_MAXM >= 256 && tiles(256, 128) >= NUM_CU / 2)
+        k = choice<256, 128, 2, 2, TG_K4_BK, TG_K4_STAGES, 2, 1, 1>(path(256, 128), NAMES_STRIP256);
+    else
 #if TG_L_CFG == 1
     if (tiles(256, 128) >= 2 * NUM_CU)
         k = choice<256, 128, 2, 2, 32, 3, 2, 2>(path(256, 128), NAMES_256x128);
@@ -1001,9 +1075,9 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
         k = choice<256, 256, 2, 2, TG_L_BK, TG_L_STAGES, TG_L_DMA_STEPS>(path(256, 256), NAMES_256);
 #endif
     else if (tiles(128, 128) >= NUM_CU)
-        k = choice<128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS>(path(128, 128), NAMES_128);
+        k = choice<128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT>(path(128, 128), NAMES_128);
     else
-        k = choice<64, 64, 2, 2, TG_S_BK, TG_S_STAGES, TG_S_DMA_STEPS>(path(64, 64), NAMES_64);
+        k = choice<64, 64, 2, 2, TG_S_BK, TG_S_STAGES, TG_S_DMA_STEPS, 1, TG_S_KROT>(path(64, 64), NAMES_64);
     Plan p;
     p.k = k;
     p.tiles_m = (int)((M + k.bm - 1) / k.bm);

@@ -95,6 +95,22 @@ def test_plans_for_workloads():
     assert name.endswith("_scalar")
 
 
+@pytest.mark.parametrize("M,N,K,tile,grid", [
+    (64, 28672, 8192, "64x128", 224),     # decode-like: one strip row, B streamed once
+    (1, 16385, 64, "64x128", 129),
+    (128, 28672, 8192, "128x128", 224),
+    (256, 28672, 8192, "256x128", 224),
+    (64, 4096, 8192, "64x64", 64),        # too few strips to fill the chip
+    (8192, 14336, 4096, "256x256", 1792),
+    (4096, 4096, 4096, "256x256", 256),
+    (2048, 2048, 2048, "128x128", 256),
+    (1000, 1000, 1000, "64x64", 256),
+])
+def test_tile_choice(M, N, K, tile, grid):
+    st, name, g = tg.tg_gemm_f16_plan(FAKE, FAKE, FAKE, M, N, K, K, K, N)
+    assert st == tg.TG_OK and name.startswith(f"gemm_f16_{tile}_") and g == grid
+
+
 def test_binding_refuses_without_library(tmp_path, monkeypatch):
     import importlib
     import dense_fp16_gemm_02_amd as pkg

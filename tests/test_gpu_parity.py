@@ -199,6 +199,38 @@ def test_large_tile_tails():
     _check(d[rows], res, "large-tails")
 
 
+@pytest.mark.parametrize("M,N,K,tile", [
+    (64, 16411, 1000, "64x128"),    # full strip, ragged N and K
+    (37, 16400, 200, "64x128"),     # ragged M; K spans 4 K-tiles (start offsets wrap)
+    (1, 16385, 64, "64x128"),       # one row; one K-tile
+    (100, 16390, 776, "128x128"),
+    (128, 16384, 1024, "128x128"),
+    (200, 16500, 512, "256x128"),
+    (256, 16384, 264, "256x128"),
+])
+def test_strip_tiles(M, N, K, tile):
+    """Small M and large N take the column-strip tiles (one tile row covers
+    M, each XCD starts at its own K offset); every element is checked."""
+    st0, name, grid = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N + 2)
+    say(f"strip plan {name} grid={grid}")
+    assert st0 == tg.TG_OK and name.startswith(f"gemm_f16_{tile}_") and name.endswith("_dma")
+    a = workloads.random_f16(300 + M, (M, K))
+    b = workloads.random_f16(400 + K, (N, K))
+    d, full, st = run(a, b, M, N, K, guard=1, label=f"strip {name}")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 1)
+    _check(d, oracle.gemm(a, b, M, N, K), f"strip {M}x{N}x{K}")
+
+
+def test_strip_index_pattern_exact():
+    """Integer operands through the strip tile with K-offset rotation: exact."""
+    M, N, K = 64, 16500, 328
+    a, b = workloads.index_pattern(M, N, K)
+    d, full, st = run(a, b, M, N, K, guard=2, label="strip index-pattern")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 2)
+    want = a.astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(d.astype(np.int64), want)
+
+
 # ------------------------------------------------------- degenerate cases
 
 def test_zero_k_gives_positive_zero():
