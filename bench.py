@@ -149,7 +149,7 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2):
         D = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
         sets.append((A, B, D))
     stream = torch.cuda.current_stream(dev)
-    st, kname, grid = tg.tg_gemm_f16_plan(A0, B0, sets[0][2], w.M, w.N, w.K, w.K, w.K, w.N)
+    st, kname, tiles = tg.tg_gemm_f16_plan(A0, B0, sets[0][2], w.M, w.N, w.K, w.K, w.K, w.N)
     if st != tg.TG_OK:
         raise RuntimeError(tg.tg_status_string(st))
 
@@ -174,7 +174,7 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2):
     ms = ev0.elapsed_time(ev1) / steps
     del sets, A0, B0
     torch.cuda.empty_cache()
-    return dict(ms=ms, wall_s=wall, kernel=kname, grid=grid, a=a, b=b)
+    return dict(ms=ms, wall_s=wall, kernel=kname, tiles=tiles, a=a, b=b)
 
 
 def cpu_baseline(w, a, b, seconds: float, rows_override=None):
@@ -263,7 +263,7 @@ def main() -> int:
     r = time_workload(w, args.steps, args.warmup)
     ms = r["ms"]
     tflops = w.flop / (ms * 1e-3) / 1e12
-    log(f"{w.name}: {r['kernel']} grid={r['grid']} {ms * 1e3:.2f} us/launch "
+    log(f"{w.name}: {r['kernel']} tiles={r['tiles']} {ms * 1e3:.2f} us/launch "
         f"{tflops:.1f} TFLOP/s ({100 * tflops / PEAK_FP16_TFLOPS:.1f}% of peak)")
 
     cpu = None
@@ -286,7 +286,7 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "kernel": r["kernel"],
-                   "grid": r["grid"], "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2)},
+                   "tiles": r["tiles"], "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic},

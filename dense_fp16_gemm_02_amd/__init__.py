@@ -5,7 +5,7 @@ kernels of ``csrc/tg_gemm.hip``.  There is no fallback: if the library is
 not built, importing the functions below raises.
 
     tg_gemm_f16(A, B, D, M, N, K, lda, ldb, ldd, stream) -> status
-    tg_gemm_f16_plan(A, B, D, M, N, K, lda, ldb, ldd) -> (status, name, grid)
+    tg_gemm_f16_plan(A, B, D, M, N, K, lda, ldb, ldd) -> (status, name, tiles)
     tg_status_string(status) -> str
     gemm(A, B, out=None, stream=None) -> D   (torch convenience wrapper)
 
@@ -88,12 +88,13 @@ def tg_gemm_f16(A, B, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int, s
 
 
 def tg_gemm_f16_plan(A, B, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int):
-    """Host-only: (status, kernel name, workgroup count) tg_gemm_f16 would use."""
+    """Host-only: (status, kernel name, output tile count) of the launch
+    tg_gemm_f16 would make."""
     buf = ctypes.create_string_buffer(128)
-    grid = ctypes.c_int64(0)
+    tiles = ctypes.c_int64(0)
     st = load().tg_gemm_f16_plan(_ptr(A), _ptr(B), _ptr(D), M, N, K, lda, ldb, ldd, buf, 128,
-                                 ctypes.byref(grid))
-    return st, buf.value.decode(), grid.value
+                                 ctypes.byref(tiles))
+    return st, buf.value.decode(), tiles.value
 
 
 def tg_status_string(status: int) -> str:

@@ -297,6 +297,14 @@ typedef __attribute__((address_space(3))) void *lds_void_ptr;
 #define TG_WAVES_PER_SIMD(n)
 #endif
 
+// Cache-policy bits of a DMA (the instruction's sc0/sc1/nt fields).  An
+// operand that every resident workgroup re-reads stays in the default
+// (cached) policy; in the column-strip tiles B is read exactly once, so its
+// loads are marked non-temporal and system-coherent-level-0 (sc0 | nt): they
+// stream past the caches instead of evicting A, which every strip re-reads.
+constexpr int CPOL_CACHED = 0;
+constexpr int CPOL_STREAM = 1 | 2;  // sc0 | nt
+
 // Raw buffer descriptor word 3 for gfx9-family GPUs (32-bit data format, no
 // swizzle, no thread-id add).  Offsets at or past DMA_RANGE bytes read zeros.
 constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
@@ -307,10 +315,11 @@ constexpr uint32_t DMA_OOB = 0x80000000u;
 // LDS bytes lds + 16·l (lds must be wave-uniform).  The builtin exists only
 // in the device pass; the host pass sees an empty body, which keeps clang
 // emitting the host-side kernel stubs.
+template <int CPOL = 0>
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, _Float16 *lds, uint32_t voff)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)lds, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)lds, 16, voff, 0, 0, CPOL);
 #else
     (void)rsrc, (void)lds, (void)voff;
 #endif
@@ -400,7 +409,7 @@ static_assert(tg::layout::check_swizzled_tile(tg::layout::swizzle_bank256_f16(25
 //   the end: an all-out-of-range DMA, i.e. a no-op that keeps the loop
 //   branch-free and the vmcnt bookkeeping uniform).
 template <int BM, int BN, int WM, int WN, int BK_, int STAGES, int OCC, int DMA_STEPS, int KROT>
-__global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC) void gemm_f16_dma_kernel(
+__global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? WM * WN / 4 : 1)) void gemm_f16_dma_kernel(
     const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
     int dvec)
@@ -486,10 +495,11 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC) void gemm_f16_d
     // i-th DMA of a K-tile: A passes first, then B passes
     auto dma_pass = [&](const DmaTile &d, int i) {
         if (i < A_PASSES)
-            dma16(d.ra, d.as + (i * NW + wave) * T::ROWS_PER_DMA * BK_,
+            dma16<CPOL_CACHED>(d.ra, d.as + (i * NW + wave) * T::ROWS_PER_DMA * BK_,
                   8 * a_kc[i] < d.klim ? a_off[i] : DMA_OOB);
         else
-            dma16(d.rb, d.bs + ((i - A_PASSES) * NW + wave) * T::ROWS_PER_DMA * BK_,
+            dma16<KROT ? CPOL_STREAM : CPOL_CACHED>(
+                d.rb, d.bs + ((i - A_PASSES) * NW + wave) * T::ROWS_PER_DMA * BK_,
                   8 * b_kc[i - A_PASSES] < d.klim ? b_off[i - A_PASSES] : DMA_OOB);
     };
 
@@ -527,14 +537,13 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC) void gemm_f16_d
     constexpr int NFRAG = TM + TN;
     constexpr int SLOTS = TM * TN;
     auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
-    // DMA passes [lo, hi) of `dma` ride along in the slots after the reads
-    // (slot NFRAG onwards when the step reads, else from slot 0), one every
-    // `every` slots.  A 1 KiB DMA blocks its wave for ~30 clocks, about the
-    // shadow of one 32-clock MFMA, so a slot never carries both a read and a
-    // DMA.
+    // DMA passes [lo, hi) of `dma` ride along from slot 1 on, one every
+    // `every` slots, so they spread evenly over the step (between and beside
+    // the fragment reads) instead of arriving at the memory pipe in a burst;
+    // passes that outnumber the slots go after the last MFMA.
     auto step = [&](const f16x8 *a, const f16x8 *b, bool with_reads, int rs, int rkk, f16x8 *na,
                     f16x8 *nb, const DmaTile *dma, int lo, int hi, int every) {
-        const int first = with_reads ? (NFRAG < SLOTS ? NFRAG : 0) : 0;
+        constexpr int first = 1;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const int ti = i / TN, tj = i % TN;
@@ -565,7 +574,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC) void gemm_f16_d
     constexpr int DSTEPS = DMA_STEPS < 1 ? 1 : DMA_STEPS > KSTEPS ? KSTEPS : DMA_STEPS;
     constexpr bool SPREAD = DSTEPS > 1;
     constexpr int P1 = (DMA_PER_TILE + DSTEPS - 1) / DSTEPS;
-    constexpr int DMA_SLOTS = NFRAG < SLOTS ? SLOTS - NFRAG : SLOTS;  // slots after the reads
+    constexpr int DMA_SLOTS = SLOTS;
     constexpr int EVERY_POST = DMA_SLOTS / P1 > 0 ? DMA_SLOTS / P1 : 1;
     constexpr int REST = DMA_PER_TILE - P1;
     constexpr int REST_PER_STEP = SPREAD ? (REST + DSTEPS - 2) / (DSTEPS - 1) : 0;
@@ -673,221 +682,6 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC) void gemm_f16_d
     }
 }
 
-// Two-wave-per-SIMD ("ping-pong") variant of the direct-to-LDS kernel.
-//
-// Eight waves share one BM×BN tile, each owning a (BM/2)×(BN/4) block of D,
-// so each SIMD hosts one wave of group 0 (waves 0-3) and one of group 1
-// (waves 4-7).  Work alternates in phases separated by workgroup barriers:
-// in every phase one group runs a MEMORY step (reads all fragments of one
-// K-tile from LDS into registers and starts its half of the DMA of a later
-// K-tile) while the other group runs a COMPUTE step (that K-tile's MFMAs
-// back to back from registers).  On each SIMD the matrix core therefore
-// always has one wave feeding it an uninterrupted MFMA stream, and the
-// memory instructions — whose issue stalls a wave while the memory pipe is
-// backed up — sit in the other wave.  This is the pages' producer/consumer
-// split ("TIRx 与高性能GEMM (上)", Step 5 and the next step it names)
-// re-planned for CDNA: both waves of a SIMD take both roles in turn, and
-// barriers with vmcnt waits replace mbarrier phases.
-//
-// Schedule (K-tile t lives in stage t mod STAGES): group 0 runs MEMORY(t) in
-// phase 2t and COMPUTE(t) in phase 2t+1; group 1 is one phase behind.  Stage
-// t mod STAGES is read in phases 2t and 2t+1, so it is free from phase 2t+2.
-// In MEMORY(t) group 0 starts the A half and group 1 the B half of the DMA
-// of K-tile t+STAGES-1 into stage (t-1) mod STAGES (free since phase 2t).
-// Before the barrier that ends phase 2t+1 every wave waits until its half of
-// K-tile t+1 has landed (its later halves, K-tiles t+2 .. t+STAGES-1, may
-// stay in flight), because group 0 reads K-tile t+1 in phase 2t+2.
-//
-// Tails, swizzle, DMA addressing and the staged epilogue are as in
-// gemm_f16_dma_kernel.
-template <int BM, int BN, int BK_, int STAGES>
-__global__ __launch_bounds__(512) TG_WAVES_PER_SIMD(2) void gemm_f16_pingpong_kernel(
-    const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
-    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
-    int dvec)
-{
-    using T = OperandTile<BK_>;
-    constexpr int WM = 2, WN = 4, NW = 8, NWG = 4;  // NWG: waves per group
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int KSTEPS = BK_ / 16;
-    // group 0 moves A, group 1 moves B; PASSES DMAs per wave and K-tile
-    constexpr int A_PASSES = BM / T::ROWS_PER_DMA / NWG, B_PASSES = BN / T::ROWS_PER_DMA / NWG;
-    static_assert(A_PASSES == B_PASSES, "both groups carry the same DMA load");
-    constexpr int PASSES = A_PASSES;
-    constexpr int STAGE = (BM + BN) * BK_;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-    static_assert((BM / T::ROWS_PER_DMA) % NWG == 0, "DMA row groups must split evenly");
-    static_assert(STAGES >= 3 && STAGES * STAGE * 2 <= 160 * 1024, "LDS budget");
-    static_assert((STAGES - 1) * PASSES <= 63, "vmcnt holds 6 bits");
-
-    __shared__ __attribute__((aligned(1024))) _Float16 smem[STAGES * STAGE];
-
-    int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int grp = wave >> 2;                   // 0 or 1
-    const int wm = wave >> 2, wn = wave & 3;     // group 0 owns rows [0, WTM), group 1 the rest
-    const int gw = wave & 3;                     // wave index inside its group
-
-    // DMA source: pass p covers operand rows t = ROWS_PER_DMA·(p·NWG + gw) +
-    // lane / RC.  Passes move t by a multiple of the swizzle period, so the
-    // swizzled chunk a lane fetches is the same in all passes.
-    static_assert((T::ROWS_PER_DMA * NWG) % (T::ROWS_PER_LINE * T::RC) == 0,
-                  "pass stride must keep the swizzle phase");
-    const int dr = lane / T::RC, dpc = lane % T::RC;
-    const int t0 = T::ROWS_PER_DMA * gw + dr;
-    const int kc = dpc ^ T::swz(t0);
-    // this group's operand: A for group 0, B for group 1
-    const int op_rows = grp == 0 ? BM : BN;
-    const int op_last = grp == 0 ? M - 1 - m0 : N - 1 - n0;
-    const int64_t op_ld = grp == 0 ? lda : ldb;
-    const char *op_tile = grp == 0 ? reinterpret_cast<const char *>(A + (int64_t)m0 * lda)
-                                   : reinterpret_cast<const char *>(B + (int64_t)n0 * ldb);
-    const int op_lds = grp == 0 ? 0 : BM * BK_;  // operand's offset inside a stage
-    (void)op_rows;
-    uint32_t off[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-        off[p] = (uint32_t)(imin(t0 + T::ROWS_PER_DMA * NWG * p, op_last) * op_ld * 2 + 16 * kc);
-    const int KT = (K + BK_ - 1) / BK_;
-
-    // this wave's share of the DMA of K-tile kt (a no-op copy of zeros when
-    // kt >= KT, which keeps the vmcnt bookkeeping uniform)
-    auto dma_half = [&](int kt) {
-        const int k = kt * BK_;
-        const bool kin = kt < KT && 8 * kc < K - k;
-        _Float16 *dst = smem + (kt % STAGES) * STAGE + op_lds;
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(op_tile + 2 * k), (short)0, DMA_RANGE, BUFFER_RSRC_WORD3);
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p)
-            dma16(r, dst + (p * NWG + gw) * T::ROWS_PER_DMA * BK_, kin ? off[p] : DMA_OOB);
-    };
-
-    const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
-    f16x8 fa[KSTEPS][TM], fb[KSTEPS][TN];
-    auto read_all = [&](int kt) {
-        const _Float16 *as = smem + (kt % STAGES) * STAGE;
-        const _Float16 *bs = as + BM * BK_;
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            const int c = kk * 2 + frag_hi;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                fa[kk][i] = *reinterpret_cast<const f16x8 *>(
-                    as + T::off(wm * WTM + i * 32 + frag_row, c));
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                fb[kk][j] = *reinterpret_cast<const f16x8 *>(
-                    bs + T::off(wn * WTN + j * 32 + frag_row, c));
-        }
-    };
-
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[i][j][v] = 0.0f;
-#if defined(__HIP_DEVICE_COMPILE__)
-    // Referencing an accumulation register makes the compiler select the
-    // AGPR form of the MFMAs: accumulators in AGPRs, fragments in VGPRs, which
-    // is what fits the 256-register budget of two waves per SIMD.
-    asm volatile("; accumulators live in AGPRs %0" ::"a"(0.0f));
-#endif
-
-    // prologue: K-tiles 0 .. STAGES-2, then wait for K-tile 0
-#pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t)
-        dma_half(t);
-    wait_vmem<(STAGES - 2) * PASSES>();
-    barrier_lds();
-
-    // Both groups run the same body, group 1 one phase behind (one extra
-    // barrier first; group 0 has one extra barrier last), so every wave
-    // passes the same number of barriers:
-    //   MEMORY(kt): read K-tile kt, start this group's half of K-tile kt+STAGES-1
-    //   COMPUTE(kt)
-    // with the "half of K-tile kt+1 has landed" wait before the barrier that
-    // ends phase 2kt+1 — after COMPUTE(kt) for group 0, after MEMORY(kt) for
-    // group 1.
-    constexpr int VM_KEEP = (STAGES - 2) * PASSES;
-    if (grp == 1)
-        barrier_lds();
-    for (int kt = 0; kt < KT; ++kt) {
-        read_all(kt);
-        dma_half(kt + STAGES - 1);
-        if (grp == 1)
-            wait_vmem<VM_KEEP>();
-        barrier_lds();
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[kk][j], fa[kk][i], acc[i][j],
-                                                                       0, 0, 0);
-        if (grp == 0)
-            wait_vmem<VM_KEEP>();
-        barrier_lds();
-    }
-    if (grp == 0)
-        barrier_lds();
-    wait_vmem<0>();
-
-    // Staged epilogue (see gemm_f16_dma_kernel), one WTM×WTN block per wave.
-    static_assert(NW * WTM * WTN <= STAGES * STAGE, "staging fits in the stage memory");
-    constexpr int SROW = WTN;
-    constexpr int SCH = WTN / 8;
-    constexpr int SRPL = (256 / 2) / SROW > 0 ? (256 / 2) / SROW : 1;  // rows per 256-byte line
-    static_assert((SCH & (SCH - 1)) == 0 && SCH >= 2, "chunk swizzle needs a power of two");
-    auto stage_off = [](int r, int chunk) {
-        return r * SROW + ((chunk ^ ((r / SRPL) & (SCH - 1))) << 3);
-    };
-    _Float16 *stg = smem + wave * WTM * WTN;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f16x4 h;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    h[r] = (_Float16)acc[i][j][g * 4 + r];  // round to nearest even
-                const int r = i * 32 + frag_row;
-                const int c = j * 32 + g * 8 + frag_hi * 4;
-                *reinterpret_cast<f16x4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
-            }
-    constexpr int ROWS_PER_PASS = 64 / SCH;
-    const int rc = lane % SCH, rr = lane / SCH;
-    const int col = n0 + wn * WTN + 8 * rc;
-#pragma unroll
-    for (int pass = 0; pass < WTM / ROWS_PER_PASS; ++pass) {
-        const int r = pass * ROWS_PER_PASS + rr;
-        const f16x8 v = *reinterpret_cast<const f16x8 *>(stg + stage_off(r, rc));
-        const int row = m0 + wm * WTM + r;
-        if (row < M) {
-            _Float16 *dst = D + (int64_t)row * ldd + col;
-            if (dvec && col + 7 < N) {
-                *reinterpret_cast<f16x8 *>(dst) = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (col + e < N)
-                        dst[e] = v[e];
-            }
-        }
-    }
-}
-
 struct KernelChoice {
     const void *fn;
     const char *name;
@@ -898,15 +692,6 @@ struct KernelChoice {
 // Compile-time tuning of the direct-to-LDS kernels: K-tile depth (BK) and
 // LDS ring depth (STAGES) per workgroup tile size (L: 256×256, M: 128×128,
 // S: 64×64).  The defaults are the measured best on MI355X.
-#ifndef TG_L_CFG
-#define TG_L_CFG 0
-#endif
-#ifndef TG_PP_BK
-#define TG_PP_BK 32
-#endif
-#ifndef TG_PP_STAGES
-#define TG_PP_STAGES 4
-#endif
 #ifndef TG_L_BK
 #define TG_L_BK 64
 #endif
@@ -960,9 +745,6 @@ KernelChoice choice(LoadPath path, const char *const names[3])
 
 constexpr const char *NAMES_256[3] = {"gemm_f16_256x256_w2x2_dma", "gemm_f16_256x256_w2x2_vec",
                                       "gemm_f16_256x256_w2x2_scalar"};
-[[maybe_unused]] constexpr const char *NAMES_256x128[3] = {"gemm_f16_256x128_w2x2_dma",
-                                          "gemm_f16_256x128_w2x2_vec",
-                                          "gemm_f16_256x128_w2x2_scalar"};
 #define TG_STR2(x) #x
 #define TG_STR(x) TG_STR2(x)
 #define TG_NAMES(bm, bn, wm, wn)                                                              \
@@ -1060,20 +842,8 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     else if (TG_K_ON && M <= 256 && TG_K_MAXM >= 256 && tiles(256, 128) >= NUM_CU / 2)
         k = choice<256, 128, 2, 2, TG_K4_BK, TG_K4_STAGES, 2, 1, 1>(path(256, 128), NAMES_STRIP256);
     else
-#if TG_L_CFG == 1
-    if (tiles(256, 128) >= 2 * NUM_CU)
-        k = choice<256, 128, 2, 2, 32, 3, 2, 2>(path(256, 128), NAMES_256x128);
-#elif TG_L_CFG == 2
-    if (tiles(256, 256) >= NUM_CU) {
-        k = choice<256, 256, 2, 2, TG_L_BK, TG_L_STAGES, TG_L_DMA_STEPS>(path(256, 256), NAMES_256);
-        if (k.path == PATH_DMA)
-            k = {reinterpret_cast<const void *>(&gemm_f16_pingpong_kernel<256, 256, TG_PP_BK, TG_PP_STAGES>),
-                 "gemm_f16_256x256_pingpong_dma", 256, 256, 512, PATH_DMA};
-    }
-#else
     if (tiles(256, 256) >= NUM_CU)
         k = choice<256, 256, 2, 2, TG_L_BK, TG_L_STAGES, TG_L_DMA_STEPS>(path(256, 256), NAMES_256);
-#endif
     else if (tiles(128, 128) >= NUM_CU)
         k = choice<128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT>(path(128, 128), NAMES_128);
     else
@@ -1137,20 +907,20 @@ extern "C" int tg_gemm_f16(const void *A, const void *B, void *D, int64_t M, int
 
 extern "C" int tg_gemm_f16_plan(const void *A, const void *B, const void *D, int64_t M,
                                 int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
-                                char *name, int64_t name_len, int64_t *grid)
+                                char *name, int64_t name_len, int64_t *tiles)
 {
     int st = validate(A, B, D, M, N, K, lda, ldb, ldd);
     if (name && name_len > 0)
         name[0] = 0;
-    if (grid)
-        *grid = 0;
+    if (tiles)
+        *tiles = 0;
     if (st != TG_OK || M == 0 || N == 0)
         return st;
     Plan p = make_plan(A, B, D, M, N, K, lda, ldb, ldd);
     if (name && name_len > 0)
         snprintf(name, (size_t)name_len, "%s", p.k.name);
-    if (grid)
-        *grid = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles)
+        *tiles = (int64_t)p.tiles_m * p.tiles_n;
     return TG_OK;
 }
 

@@ -75,16 +75,17 @@ int tg_gemm_f16(const void *A, const void *B, void *D,
 
 /*
  * tg_gemm_f16_plan — host-only: the name of the kernel tg_gemm_f16 would
- * launch for these arguments, and its grid, without touching the device.
- * Writes a NUL-terminated name of at most `name_len` bytes into `name`
- * (may be NULL) and the workgroup count into *grid (may be NULL; 0 when
- * nothing would be launched).  Returns the status tg_gemm_f16 would return
- * for argument validation (TG_OK, TG_ERR_INVALID_ARG or TG_ERR_TOO_LARGE).
+ * launch for these arguments, and the number of output tiles it splits D
+ * into, without touching the device.  Writes a NUL-terminated name of at
+ * most `name_len` bytes into `name` (may be NULL) and the tile count into
+ * *tiles (may be NULL; 0 when nothing would be launched); the launch has
+ * one workgroup per tile.  Returns the status tg_gemm_f16 would return for
+ * argument validation (TG_OK, TG_ERR_INVALID_ARG or TG_ERR_TOO_LARGE).
  */
 int tg_gemm_f16_plan(const void *A, const void *B, const void *D,
                      int64_t M, int64_t N, int64_t K,
                      int64_t lda, int64_t ldb, int64_t ldd,
-                     char *name, int64_t name_len, int64_t *grid);
+                     char *name, int64_t name_len, int64_t *tiles);
 
 /* tg_status_string — a static, NUL-terminated description of a status. */
 const char *tg_status_string(int status);

@@ -56,8 +56,8 @@ FAKE = 1 << 20  # a non-NULL pointer value; validation rejects before any use
 ])
 def test_invalid_arguments_rejected_without_launch(args):
     assert tg.tg_gemm_f16(*args, None) == tg.TG_ERR_INVALID_ARG
-    st, name, grid = tg.tg_gemm_f16_plan(*args)
-    assert st == tg.TG_ERR_INVALID_ARG and name == "" and grid == 0
+    st, name, tiles = tg.tg_gemm_f16_plan(*args)
+    assert st == tg.TG_ERR_INVALID_ARG and name == "" and tiles == 0
 
 
 def test_too_large_rejected():
@@ -85,9 +85,9 @@ def test_status_strings():
 
 def test_plans_for_workloads():
     for w in workloads.WORKLOADS:
-        st, name, grid = tg.tg_gemm_f16_plan(FAKE, FAKE, FAKE, w.M, w.N, w.K, w.K, w.K, w.N)
+        st, name, tiles = tg.tg_gemm_f16_plan(FAKE, FAKE, FAKE, w.M, w.N, w.K, w.K, w.K, w.N)
         assert st == tg.TG_OK and name.startswith("gemm_f16_") and name.endswith("_dma")
-        assert grid > 0
+        assert tiles > 0
     # misaligned pointer or K % 8 != 0 takes the element-wise path
     st, name, _ = tg.tg_gemm_f16_plan(FAKE + 2, FAKE, FAKE, 64, 64, 64, 64, 64, 64)
     assert name.endswith("_scalar")
@@ -95,7 +95,7 @@ def test_plans_for_workloads():
     assert name.endswith("_scalar")
 
 
-@pytest.mark.parametrize("M,N,K,tile,grid", [
+@pytest.mark.parametrize("M,N,K,tile,tiles", [
     (64, 28672, 8192, "64x128", 224),     # decode-like: one strip row, B streamed once
     (1, 16385, 64, "64x128", 129),
     (128, 28672, 8192, "128x128", 224),
@@ -106,9 +106,9 @@ def test_plans_for_workloads():
     (2048, 2048, 2048, "128x128", 256),
     (1000, 1000, 1000, "64x64", 256),
 ])
-def test_tile_choice(M, N, K, tile, grid):
+def test_tile_choice(M, N, K, tile, tiles):
     st, name, g = tg.tg_gemm_f16_plan(FAKE, FAKE, FAKE, M, N, K, K, K, N)
-    assert st == tg.TG_OK and name.startswith(f"gemm_f16_{tile}_") and g == grid
+    assert st == tg.TG_OK and name.startswith(f"gemm_f16_{tile}_") and g == tiles
 
 
 def test_binding_refuses_without_library(tmp_path, monkeypatch):

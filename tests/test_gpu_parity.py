@@ -189,8 +189,8 @@ def test_large_tile_tails():
     M, N, K = 4100, 4200, 1000
     a = workloads.random_f16(91, (M, K))
     b = workloads.random_f16(92, (N, K))
-    st0, name, grid = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N)
-    say(f"large tails plan {name} grid={grid}")
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N)
+    say(f"large tails plan {name} tiles={tiles}")
     d, full, st = run(a, b, M, N, K, guard=2, label="large-tails")
     assert st == tg.TG_OK and guard_intact(full, M, N, 2)
     rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(M - 300, M),
@@ -211,8 +211,8 @@ def test_large_tile_tails():
 def test_strip_tiles(M, N, K, tile):
     """Small M and large N take the column-strip tiles (one tile row covers
     M, each XCD starts at its own K offset); every element is checked."""
-    st0, name, grid = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N + 2)
-    say(f"strip plan {name} grid={grid}")
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N + 2)
+    say(f"strip plan {name} tiles={tiles}")
     assert st0 == tg.TG_OK and name.startswith(f"gemm_f16_{tile}_") and name.endswith("_dma")
     a = workloads.random_f16(300 + M, (M, K))
     b = workloads.random_f16(400 + K, (N, K))
@@ -229,6 +229,37 @@ def test_strip_index_pattern_exact():
     assert st == tg.TG_OK and guard_intact(full, M, N, 2)
     want = a.astype(np.int64) @ b.astype(np.int64).T
     assert np.array_equal(d.astype(np.int64), want)
+
+
+def test_persistent_tiles_exact():
+    """More 256×256 tiles than resident workgroups (17×17 = 289): workgroups
+    take a second tile whose first K-tiles load during the first tile's
+    epilogue.  Integer operands: every checked element is exact."""
+    M, N, K = 4352 - 5, 4352 - 3, 136
+    a, b = workloads.index_pattern(M, N, K)
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N + 2)
+    say(f"persistent plan {name} tiles={tiles}")
+    assert name.startswith("gemm_f16_256x256_") and tiles == 289
+    d, full, st = run(a, b, M, N, K, guard=1, label="persistent exact")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 1)
+    rows = np.unique(np.concatenate([np.arange(0, 300), np.arange(M - 300, M),
+                                     np.arange(2048 - 8, 2048 + 8)]))
+    want = a[rows].astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(d[rows].astype(np.int64), want)
+
+
+def test_persistent_zero_k():
+    """K = 0 with more tiles than resident workgroups: every tile is +0."""
+    M, N = 4352, 4352
+    # lda = ldb = 8 keeps the direct-to-LDS kernel; the NaN columns are never read
+    a = np.full((M, 8), np.nan, dtype=np.float16)
+    b = np.full((N, 8), np.nan, dtype=np.float16)
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, 0, 8, 8, N + 2)
+    say(f"persistent K=0 plan {name} tiles={tiles}")
+    assert name.endswith("_dma") and tiles == 289
+    d, full, st = run(a, b, M, N, 0, guard=1, label="persistent K=0")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 1)
+    assert np.all(_bits(d) == 0)
 
 
 # ------------------------------------------------------- degenerate cases
