@@ -131,7 +131,7 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_workload(w, steps: int, warmup: int, rotate: int = 2):
+def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = False):
     import numpy as np
     import torch
 
@@ -155,6 +155,9 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2):
 
     def step(i):
         A, B, D = sets[i % rotate]
+        if vendor:  # context only: the vendor library on the same inputs
+            torch.matmul(A, B.t(), out=D)
+            return
         s = tg.tg_gemm_f16(A, B, D, w.M, w.N, w.K, w.K, w.K, w.N, stream)
         if s != tg.TG_OK:
             raise RuntimeError(f"tg_gemm_f16: {tg.tg_status_string(s)}")
@@ -220,6 +223,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and print a table on stderr")
+    ap.add_argument("--vendor", action="store_true",
+                    help="with --all: also time torch.matmul on the same inputs (context)")
     ap.add_argument("--copy-bytes", type=int, default=None,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--traffic-record", nargs=4, metavar="CSV", default=None,
@@ -259,6 +264,11 @@ def main() -> int:
             gbs = ww.min_bytes / (r["ms"] * 1e-3) / 1e9
             log(f"{ww.name:28s} {r['kernel']:32s} {r['ms'] * 1e3:9.2f} {tf:9.1f} "
                 f"{100 * tf / PEAK_FP16_TFLOPS:7.2f} {gbs:8.0f}")
+            if args.vendor:
+                v = time_workload(ww, args.steps, args.warmup, vendor=True)
+                tfv = ww.flop / (v["ms"] * 1e-3) / 1e12
+                log(f"{'':28s} {'torch.matmul':32s} {v['ms'] * 1e3:9.2f} {tfv:9.1f} "
+                    f"{100 * tfv / PEAK_FP16_TFLOPS:7.2f} {ww.min_bytes / (v['ms'] * 1e-3) / 1e9:8.0f}")
 
     r = time_workload(w, args.steps, args.warmup)
     ms = r["ms"]

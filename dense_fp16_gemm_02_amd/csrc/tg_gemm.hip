@@ -72,7 +72,8 @@ static_assert(tg::layout::check_acc_fragment(acc_row_of, acc_col_of),
 // each XCD gets a contiguous range of logical tile ids, and logical ids walk
 // groups of GROUP_M tile rows column by column (the grouped order of the
 // pages' persistent scheduler), so the workgroups resident on one XCD share
-// A and B bands in that XCD's L2.
+// A and B bands in that XCD's L2; group g starts its column walk at column
+// g·tiles_n/8.
 constexpr int NUM_XCD = 8;
 #ifndef TG_GROUP_M
 #define TG_GROUP_M 4
@@ -92,7 +93,14 @@ __host__ __device__ constexpr void tile_of(int bid, int tiles_m, int tiles_n, in
     const int rows_in_group = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
     const int in_group = logical - group * group_size;
     tm = first_m + in_group % rows_in_group;
-    tn = in_group / rows_in_group;
+    // Each group walks the columns from its own starting point, spread over
+    // the row of tiles, so that the XCDs (which hold consecutive groups)
+    // stream different B bands at any moment rather than all requesting the
+    // same one.
+    const int start = (int)((int64_t)group * tiles_n / NUM_XCD % tiles_n);
+    tn = in_group / rows_in_group + start;
+    if (tn >= tiles_n)
+        tn -= tiles_n;
 }
 
 // Every workgroup id in [0, tiles_m·tiles_n) maps to a distinct tile inside
