@@ -310,6 +310,9 @@ typedef __attribute__((address_space(3))) void *lds_void_ptr;
 // (cached) policy; in the column-strip tiles B is read exactly once, so its
 // loads are marked non-temporal and system-coherent-level-0 (sc0 | nt): they
 // stream past the caches instead of evicting A, which every strip re-reads.
+// Fence after each slot's MFMA: the MFMA issues first and its companions
+// (fragment reads, DMAs) issue in its shadow, never ahead of it.
+#define MFMA_FIRST() __builtin_amdgcn_sched_barrier(0)
 constexpr int CPOL_CACHED = 0;
 constexpr int CPOL_STREAM = 1 | 2;  // sc0 | nt
 
@@ -556,6 +559,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
         for (int i = 0; i < SLOTS; ++i) {
             const int ti = i / TN, tj = i % TN;
             acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[tj], a[ti], acc[ti][tj], 0, 0, 0);
+            MFMA_FIRST();
             if (with_reads && i < NFRAG)
                 read_frag(rs, rkk, frag_of_slot(i), na, nb);
             if (dma && i >= first && (i - first) % every == 0 && lo + (i - first) / every < hi)
@@ -690,6 +694,256 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
     }
 }
 
+// Variant of gemm_f16_dma_kernel for the largest tile with separate LDS rings
+// for the two operands: three stages of A and two of B (BK = 64: 3·32 + 2·32
+// KiB = 160 KiB for 256×256).  With one ring of two stages the refill of a
+// drained stage has one K-tile to land, so its 16 DMAs per wave had to be
+// packed into two of the four K-steps, where they saturate the CU's address
+// unit (64 bytes per clock) and stall the wave's in-order issue behind it,
+// MFMAs included.  The third A stage gives A's refill two K-tiles, so each of
+// the four K-steps now carries four DMAs per wave: B's refill in the last
+// K-step of a tile and the first of the next (same latency budget as before),
+// A's refill, one K-tile further ahead, in the next two.  Per iteration t:
+//   K-step 0: B(t+1), second half      K-step 1: A(t+2), first half
+//   K-step 2: A(t+2), second half      wait until all but A(t+2) landed
+//   barrier (A stage t mod 3 and B stage t mod 2 are drained)
+//   K-step 3: B(t+2), first half (and the fragments of K-tile t+1, step 0)
+// Everything else (swizzle, fragment reads, tails, staged epilogue) is as in
+// gemm_f16_dma_kernel; rows past M or N are clamped.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma3_kernel(
+    const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
+    int dvec)
+{
+    constexpr int BK_ = 64, SA = 3, SB = 2;
+    using T = OperandTile<BK_>;
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int KSTEPS = BK_ / 16;
+    constexpr int A_PASSES = BM / T::ROWS_PER_DMA / NW, B_PASSES = BN / T::ROWS_PER_DMA / NW;
+    constexpr int AH = A_PASSES / 2, BH = B_PASSES / 2;
+    constexpr int STAGE_A = BM * BK_, STAGE_B = BN * BK_;
+    static_assert(KSTEPS == 4 && A_PASSES % 2 == 0 && B_PASSES % 2 == 0, "schedule assumes 4 K-steps");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert((BM / T::ROWS_PER_DMA) % NW == 0 && (BN / T::ROWS_PER_DMA) % NW == 0,
+                  "DMA row groups must split evenly over the waves");
+    static_assert((SA * STAGE_A + SB * STAGE_B) * 2 <= 160 * 1024, "LDS budget");
+    static_assert(A_PASSES + BH + A_PASSES <= 63, "vmcnt holds 6 bits");
+
+    __shared__ __attribute__((aligned(1024))) _Float16 smem[SA * STAGE_A + SB * STAGE_B];
+    _Float16 *const a_ring = smem;
+    _Float16 *const b_ring = smem + SA * STAGE_A;
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    const int dr = lane / T::RC, dpc = lane % T::RC;
+    uint32_t a_off[A_PASSES], b_off[B_PASSES];
+    int a_kc[A_PASSES], b_kc[B_PASSES];
+#pragma unroll
+    for (int p = 0; p < A_PASSES; ++p) {
+        const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
+        a_kc[p] = dpc ^ T::swz(t);
+        a_off[p] = (uint32_t)(imin(t, M - 1 - m0) * lda * 2 + 16 * a_kc[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < B_PASSES; ++p) {
+        const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
+        b_kc[p] = dpc ^ T::swz(t);
+        b_off[p] = (uint32_t)(imin(t, N - 1 - n0) * ldb * 2 + 16 * b_kc[p]);
+    }
+    const char *a_tile = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
+    const char *b_tile = reinterpret_cast<const char *>(B + (int64_t)n0 * ldb);
+    const int KT = (K + BK_ - 1) / BK_;
+
+    // DMA source and LDS stage of one operand's K-tile
+    struct Op {
+        __amdgpu_buffer_rsrc_t r;
+        _Float16 *dst;
+        int klim;  // valid K elements (0 past the end)
+    };
+    auto op_a = [&](int t) {
+        const int k = t * BK_;
+        Op o;
+        o.r = __builtin_amdgcn_make_buffer_rsrc((void *)(a_tile + 2 * k), (short)0, DMA_RANGE,
+                                                BUFFER_RSRC_WORD3);
+        o.dst = a_ring + (t % SA) * STAGE_A;
+        o.klim = t < KT ? K - k : 0;
+        return o;
+    };
+    auto op_b = [&](int t) {
+        const int k = t * BK_;
+        Op o;
+        o.r = __builtin_amdgcn_make_buffer_rsrc((void *)(b_tile + 2 * k), (short)0, DMA_RANGE,
+                                                BUFFER_RSRC_WORD3);
+        o.dst = b_ring + (t % SB) * STAGE_B;
+        o.klim = t < KT ? K - k : 0;
+        return o;
+    };
+    auto dma_a = [&](const Op &o, int p) {
+        dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BK_,
+                           8 * a_kc[p] < o.klim ? a_off[p] : DMA_OOB);
+    };
+    auto dma_b = [&](const Op &o, int p) {
+        dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BK_,
+                           8 * b_kc[p] < o.klim ? b_off[p] : DMA_OOB);
+    };
+
+    const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
+    f16x8 fa[2][TM], fb[2][TN];
+    // fragment q of K-step kk of the K-tile in A stage sa / B stage sb
+    auto read_frag = [&](int sa, int sb, int kk, int q, f16x8 *a, f16x8 *b) {
+        const int c = kk * 2 + frag_hi;
+        if (q < TM)
+            a[q] = *reinterpret_cast<const f16x8 *>(a_ring + sa * STAGE_A +
+                                                    T::off(wm * WTM + q * 32 + frag_row, c));
+        else
+            b[q - TM] = *reinterpret_cast<const f16x8 *>(
+                b_ring + sb * STAGE_B + T::off(wn * WTN + (q - TM) * 32 + frag_row, c));
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[i][j][v] = 0.0f;
+
+    constexpr int NFRAG = TM + TN;
+    constexpr int SLOTS = TM * TN;
+    auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
+    // One K-step: MFMA per slot; the next step's read i after MFMA i (i <
+    // NFRAG); the DMA passes [lo, hi) of `o` (A when is_a) from slot 1 at an
+    // even stride; passes that outnumber the slots go after the last MFMA.
+    auto step = [&](const f16x8 *a, const f16x8 *b, bool with_reads, int rsa, int rsb, int rkk,
+                    f16x8 *na, f16x8 *nb, const Op *o, bool is_a, int lo, int hi) {
+        const int n = hi - lo;
+        const int every = n > 0 && SLOTS / n > 0 ? SLOTS / n : 1;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int ti = i / TN, tj = i % TN;
+            acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[tj], a[ti], acc[ti][tj], 0, 0, 0);
+            MFMA_FIRST();
+            if (with_reads && i < NFRAG)
+                read_frag(rsa, rsb, rkk, frag_of_slot(i), na, nb);
+            if (o && i >= 1 && (i - 1) % every == 0 && lo + (i - 1) / every < hi) {
+                if (is_a)
+                    dma_a(*o, lo + (i - 1) / every);
+                else
+                    dma_b(*o, lo + (i - 1) / every);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = SLOTS; i < NFRAG; ++i)
+            if (with_reads)
+                read_frag(rsa, rsb, rkk, frag_of_slot(i), na, nb);
+        if (o)
+            for (int p = lo + (SLOTS - 1 + every - 1) / every; p < hi; ++p) {
+                if (is_a)
+                    dma_a(*o, p);
+                else
+                    dma_b(*o, p);
+            }
+    };
+
+    // prologue: A(0), B(0), A(1), first half of B(1); wait for A(0) and B(0)
+    {
+        const Op a0 = op_a(0), b0 = op_b(0), a1 = op_a(1), b1 = op_b(1);
+#pragma unroll
+        for (int p = 0; p < A_PASSES; ++p)
+            dma_a(a0, p);
+#pragma unroll
+        for (int p = 0; p < B_PASSES; ++p)
+            dma_b(b0, p);
+#pragma unroll
+        for (int p = 0; p < A_PASSES; ++p)
+            dma_a(a1, p);
+#pragma unroll
+        for (int p = 0; p < BH; ++p)
+            dma_b(b1, p);
+    }
+    wait_vmem<A_PASSES + BH>();
+    barrier_lds();
+#pragma unroll
+    for (int q = 0; q < NFRAG; ++q)
+        read_frag(0, 0, 0, q, fa[0], fb[0]);
+
+    int sa = 0, sb = 0;  // stages of K-tile kt
+    for (int kt = 0; kt < KT - 1; ++kt) {
+        const Op bn = op_b(kt + 1), an = op_a(kt + 2);
+        step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], &bn, false, BH, B_PASSES);
+        step(fa[1], fb[1], true, sa, sb, 2, fa[0], fb[0], &an, true, 0, AH);
+        step(fa[0], fb[0], true, sa, sb, 3, fa[1], fb[1], &an, true, AH, A_PASSES);
+        wait_vmem<A_PASSES>();  // K-tile kt+1 has landed (this wave's part); A(kt+2) may not
+        barrier_lds();          // ... for every wave; A stage sa and B stage sb are drained
+        const Op b2 = op_b(kt + 2);
+        const int sa1 = sa + 1 == SA ? 0 : sa + 1, sb1 = sb + 1 == SB ? 0 : sb + 1;
+        step(fa[1], fb[1], true, sa1, sb1, 0, fa[0], fb[0], &b2, false, 0, BH);
+        sa = sa1;
+        sb = sb1;
+    }
+    if (KT > 0) {
+        step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], nullptr, false, 0, 0);
+        step(fa[1], fb[1], true, sa, sb, 2, fa[0], fb[0], nullptr, false, 0, 0);
+        step(fa[0], fb[0], true, sa, sb, 3, fa[1], fb[1], nullptr, false, 0, 0);
+        step(fa[1], fb[1], false, 0, 0, 0, fa[0], fb[0], nullptr, false, 0, 0);
+    }
+    wait_vmem<0>();  // no LDS DMA may be outstanding when the wave ends
+
+    // staged epilogue, as in gemm_f16_dma_kernel
+    static_assert(NW * WTM * WTN <= SA * STAGE_A + SB * STAGE_B, "staging fits in the stage memory");
+    constexpr int SROW = WTN;
+    constexpr int SCH = WTN / 8;
+    static_assert((SCH & (SCH - 1)) == 0 && SCH >= 2, "chunk swizzle needs a power of two");
+    auto stage_off = [](int r, int chunk) { return r * SROW + ((chunk ^ (r & (SCH - 1))) << 3); };
+    barrier_lds();
+    _Float16 *stg = smem + wave * WTM * WTN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f16x4 h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    h[r] = (_Float16)acc[i][j][g * 4 + r];  // round to nearest even
+                const int r = i * 32 + frag_row;
+                const int c = j * 32 + g * 8 + frag_hi * 4;
+                *reinterpret_cast<f16x4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
+            }
+    constexpr int ROWS_PER_PASS = 64 / SCH;
+    const int rc = lane % SCH, rr = lane / SCH;
+    const int col = n0 + wn * WTN + 8 * rc;
+#pragma unroll
+    for (int pass = 0; pass < WTM / ROWS_PER_PASS; ++pass) {
+        const int r = pass * ROWS_PER_PASS + rr;
+        const f16x8 v = *reinterpret_cast<const f16x8 *>(stg + stage_off(r, rc));
+        const int row = m0 + wm * WTM + r;
+        if (row < M) {
+            _Float16 *dst = D + (int64_t)row * ldd + col;
+            if (dvec && col + 7 < N) {
+                *reinterpret_cast<f16x8 *>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < N)
+                        dst[e] = v[e];
+            }
+        }
+    }
+}
+
 struct KernelChoice {
     const void *fn;
     const char *name;
@@ -697,18 +951,10 @@ struct KernelChoice {
     int path;
 };
 
-// Compile-time tuning of the direct-to-LDS kernels: K-tile depth (BK) and
-// LDS ring depth (STAGES) per workgroup tile size (L: 256×256, M: 128×128,
-// S: 64×64).  The defaults are the measured best on MI355X.
-#ifndef TG_L_BK
-#define TG_L_BK 64
-#endif
-#ifndef TG_L_STAGES
-#define TG_L_STAGES 2
-#endif
-#ifndef TG_L_DMA_STEPS
-#define TG_L_DMA_STEPS 2
-#endif
+// Compile-time tuning of the direct-to-LDS kernels: K-tile depth (BK), LDS
+// ring depth (STAGES) and DMA spread per workgroup tile size (M: 128×128,
+// S: 64×64, K*: column strips; the 256×256 tile uses gemm_f16_dma3_kernel).
+// The defaults are the measured best on MI355X.
 #ifndef TG_M_DMA_STEPS
 #define TG_M_DMA_STEPS 1
 #endif
@@ -850,8 +1096,14 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     else if (TG_K_ON && M <= 256 && TG_K_MAXM >= 256 && tiles(256, 128) >= NUM_CU / 2)
         k = choice<256, 128, 2, 2, TG_K4_BK, TG_K4_STAGES, 2, 1, 1>(path(256, 128), NAMES_STRIP256);
     else
-    if (tiles(256, 256) >= NUM_CU)
-        k = choice<256, 256, 2, 2, TG_L_BK, TG_L_STAGES, TG_L_DMA_STEPS>(path(256, 256), NAMES_256);
+    if (tiles(256, 256) >= NUM_CU) {
+        const LoadPath lp = path(256, 256);
+        if (lp == PATH_DMA)
+            k = {reinterpret_cast<const void *>(&gemm_f16_dma3_kernel<256, 256, 2, 2>),
+                 NAMES_256[PATH_DMA], 256, 256, 256, PATH_DMA};
+        else
+            k = choice<256, 256, 2, 2, 64, 2>(lp, NAMES_256);
+    }
     else if (tiles(128, 128) >= NUM_CU)
         k = choice<128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT>(path(128, 128), NAMES_128);
     else
