@@ -820,6 +820,9 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
 
     constexpr int NFRAG = TM + TN;
     constexpr int SLOTS = TM * TN;
+    // fragment reads every other slot, DMAs in the odd slots between them:
+    // the LDS sees reads and DMA writes interleaved rather than in bursts
+    constexpr int RSTRIDE = 2;
     auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
     // One K-step: MFMA per slot; the next step's read i after MFMA i (i <
     // NFRAG); the DMA passes [lo, hi) of `o` (A when is_a) from slot 1 at an
@@ -833,8 +836,8 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
             const int ti = i / TN, tj = i % TN;
             acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[tj], a[ti], acc[ti][tj], 0, 0, 0);
             MFMA_FIRST();
-            if (with_reads && i < NFRAG)
-                read_frag(rsa, rsb, rkk, frag_of_slot(i), na, nb);
+            if (with_reads && i % RSTRIDE == 0 && i / RSTRIDE < NFRAG)
+                read_frag(rsa, rsb, rkk, frag_of_slot(i / RSTRIDE), na, nb);
             if (o && i >= 1 && (i - 1) % every == 0 && lo + (i - 1) / every < hi) {
                 if (is_a)
                     dma_a(*o, lo + (i - 1) / every);
@@ -844,9 +847,9 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = SLOTS; i < NFRAG; ++i)
+        for (int q = (SLOTS + RSTRIDE - 1) / RSTRIDE; q < NFRAG; ++q)
             if (with_reads)
-                read_frag(rsa, rsb, rkk, frag_of_slot(i), na, nb);
+                read_frag(rsa, rsb, rkk, frag_of_slot(q), na, nb);
         if (o)
             for (int p = lo + (SLOTS - 1 + every - 1) / every; p < hi; ++p) {
                 if (is_a)
