@@ -1,4 +1,4 @@
-"""CPU oracle for the fp16 GEMM D = A·Bᵀ — test infrastructure only.
+"""CPU oracle for the fp16 (and bf16) GEMM D = A·Bᵀ — test infrastructure only.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg may import this package.  The GPU library never does,
@@ -10,7 +10,11 @@ with ctypes and adds the acceptance check used by the parity tests.
 
 Acceptance (per checked element): |D − ref| ≤ 4e-3·bound + ulp16(ref) and D
 finite, where bound = Σ_k |A_ik|·|B_jk| and ulp16(x) is the spacing of
-binary16 at |x|: 2^(⌊log2|x|⌋−10) for |x| ≥ 2^−14, else 2^−24.
+binary16 at |x|: 2^(⌊log2|x|⌋−10) for |x| ≥ 2^−14, else 2^−24.  For bfloat16
+the output term is ulp_bf16(ref) = 2^(⌊log2|x|⌋−7) (2^−133 below 2^−126).
+
+bfloat16 arrays are passed and returned as uint16 bit patterns (numpy has no
+bfloat16 type); ``fmt="bf16"`` selects that format everywhere.
 """
 from __future__ import annotations
 
@@ -59,9 +63,14 @@ def _load():
     lib.oracle_half_to_double_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
     lib.oracle_double_to_half_array.restype = None
     lib.oracle_double_to_half_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
-    lib.oracle_gemm_f16.restype = ctypes.c_int
-    lib.oracle_gemm_f16.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
-        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+    lib.oracle_bf16_to_double_array.restype = None
+    lib.oracle_bf16_to_double_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+    lib.oracle_double_to_bf16_array.restype = None
+    lib.oracle_double_to_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+    for fn in (lib.oracle_gemm_f16, lib.oracle_gemm_bf16):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -89,25 +98,56 @@ def double_to_half_bits(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def bf16_to_double(h: np.ndarray) -> np.ndarray:
+    """Exact bfloat16 (uint16 bits) → float64 decode."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float64)
+    _load().oracle_bf16_to_double_array(h.ctypes.data, out.ctypes.data, h.size)
+    return out
+
+
+def double_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 → bfloat16 bits, round-to-nearest-even from float64."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_double_to_bf16_array(x.ctypes.data, out.ctypes.data, x.size)
+    return out
+
+
+def decode(x: np.ndarray, fmt: str) -> np.ndarray:
+    """float64 values of fp16 data (fmt "f16") or bf16 bit patterns ("bf16")."""
+    if fmt == "bf16":
+        return bf16_to_double(x)
+    return np.asarray(x, dtype=np.float16).astype(np.float64)
+
+
 class Result:
     """Oracle output for the requested rows: fp16 D, fp64 bound and fp64 sum."""
 
-    def __init__(self, d: np.ndarray, bound: np.ndarray, total: np.ndarray, rows: np.ndarray):
-        self.d = d
+    def __init__(self, d: np.ndarray, bound: np.ndarray, total: np.ndarray, rows: np.ndarray,
+                 fmt: str = "f16"):
+        self.d = d          # float16 values, or uint16 bf16 bit patterns
         self.bound = bound
         self.sum = total
         self.rows = rows
+        self.fmt = fmt
 
 
 def gemm(a: np.ndarray, b: np.ndarray, M: int, N: int, K: int,
-         rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None) -> Result:
-    """Reference D = A·Bᵀ on fp16 arrays ``a`` (M×lda) and ``b`` (N×ldb).
+         rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None,
+         fmt: str = "f16") -> Result:
+    """Reference D = A·Bᵀ on fp16 arrays ``a`` (M×lda) and ``b`` (N×ldb), or
+    on bf16 bit arrays with ``fmt="bf16"``.
 
     Returns the requested rows (all rows if ``rows`` is None) as a dense
-    (len(rows), N) float16 array, with bound and the fp64 sum beside it.
+    (len(rows), N) float16 array (uint16 bf16 bits for bf16), with bound and
+    the fp64 sum beside it.
     """
-    a = np.ascontiguousarray(a, dtype=np.float16)
-    b = np.ascontiguousarray(b, dtype=np.float16)
+    if fmt not in ("f16", "bf16"):
+        raise ValueError("fmt must be 'f16' or 'bf16'")
+    et = np.uint16 if fmt == "bf16" else np.float16
+    a = np.ascontiguousarray(a, dtype=et)
+    b = np.ascontiguousarray(b, dtype=et)
     if a.ndim != 2 or b.ndim != 2 or a.shape[0] < M or b.shape[0] < N:
         raise ValueError("operand shapes do not cover M/N")
     lda, ldb = a.shape[1], b.shape[1]
@@ -121,11 +161,12 @@ def gemm(a: np.ndarray, b: np.ndarray, M: int, N: int, K: int,
     else:
         rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
         nrows = rows_arr.size
-    d = np.zeros((nrows, N), dtype=np.float16)
+    d = np.zeros((nrows, N), dtype=et)
     bound = np.zeros((nrows, N), dtype=np.float64)
     total = np.zeros((nrows, N), dtype=np.float64)
     nt = default_threads() if nthreads is None else nthreads
-    rc = _load().oracle_gemm_f16(
+    fn = _load().oracle_gemm_bf16 if fmt == "bf16" else _load().oracle_gemm_f16
+    rc = fn(
         a.ctypes.data if a.size else None, b.ctypes.data if b.size else None,
         d.ctypes.data if d.size else None, bound.ctypes.data if bound.size else None,
         total.ctypes.data if total.size else None,
@@ -135,7 +176,7 @@ def gemm(a: np.ndarray, b: np.ndarray, M: int, N: int, K: int,
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     out_rows = np.arange(M, dtype=np.int64) if rows is None else rows_arr
-    return Result(d, bound, total, out_rows)
+    return Result(d, bound, total, out_rows, fmt)
 
 
 def ulp16(x: np.ndarray) -> np.ndarray:
@@ -149,8 +190,21 @@ def ulp16(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def tolerance(ref_f16: np.ndarray, bound: np.ndarray) -> np.ndarray:
-    return REL_TOL * bound + ulp16(ref_f16.astype(np.float64))
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 at |x| (2^-133 in the subnormal range and at 0)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    out = np.full(ax.shape, 2.0 ** -133)
+    big = ax >= 2.0 ** -126
+    if np.any(big):
+        e = np.floor(np.log2(ax[big]))
+        out[big] = np.exp2(e - 7)
+    return out
+
+
+def tolerance(ref: np.ndarray, bound: np.ndarray, fmt: str = "f16") -> np.ndarray:
+    if fmt == "bf16":
+        return REL_TOL * bound + ulp_bf16(bf16_to_double(ref))
+    return REL_TOL * bound + ulp16(ref.astype(np.float64))
 
 
 def check(d_gpu: np.ndarray, res: Result, cols: Optional[np.ndarray] = None):
@@ -159,15 +213,15 @@ def check(d_gpu: np.ndarray, res: Result, cols: Optional[np.ndarray] = None):
     report) where worst_ratio = max |D−ref| / tol (≤ 1 passes)."""
     ref = res.d if cols is None else res.d[:, cols]
     bound = res.bound if cols is None else res.bound[:, cols]
-    d = np.asarray(d_gpu, dtype=np.float16)
+    d = np.asarray(d_gpu, dtype=np.uint16 if res.fmt == "bf16" else np.float16)
     if d.shape != ref.shape:
         raise ValueError(f"shape mismatch {d.shape} vs {ref.shape}")
     if d.size == 0:
         return True, 0.0, "empty"
-    dd = d.astype(np.float64)
-    rr = ref.astype(np.float64)
+    dd = decode(d, res.fmt)
+    rr = decode(ref, res.fmt)
     finite = np.isfinite(dd)
-    tol = tolerance(ref, bound)
+    tol = tolerance(ref, bound, res.fmt)
     err = np.abs(dd - rr)
     err = np.where(finite, err, np.inf)
     ratio = err / tol

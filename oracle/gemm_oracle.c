@@ -20,6 +20,12 @@
  *
  * Layout: A[i,k] = A[i*lda + k], B[j,k] = B[j*ldb + k], row-major, leading
  * dimensions in elements.  Outputs are dense (rows × N).
+ *
+ * bfloat16 variant ("从编译器能力到公开算子", section "SM90a 支持具体补了什么":
+ * the matrix-multiply path takes FP16 or BF16 inputs with FP32
+ * accumulation): the same definition with bfloat16 operands and output.  The
+ * pages do not name the output rounding for BF16; the reading taken is the
+ * fp16 one, round-to-nearest-even, applied directly from the float64 sum.
  */
 #include <math.h>
 #include <pthread.h>
@@ -83,6 +89,75 @@ uint16_t oracle_double_to_half(double x)
     return (uint16_t)(sign | n);
 }
 
+/* bfloat16 → float64, exact.  Sign bit 15, exponent bits 14..7 (bias 127,
+ * the binary32 range), fraction bits 6..0; exponent 0 is the subnormal
+ * range f·2^-133. */
+double oracle_bf16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int f = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x80), e - 134);
+    return sign ? -v : v;
+}
+
+/* float64 → bfloat16, round-to-nearest, ties to even, directly from the
+ * float64 value (the same construction as the binary16 one: scale to the
+ * ulp at |x|, round the integer, renormalize).  Overflow to ±inf at and
+ * above 2^128·(1 − 2^-9), NaN stays NaN, subnormals are kept. */
+uint16_t oracle_double_to_bf16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7fc0);
+    double a = fabs(x);
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7f80);
+    if (a == 0.0)
+        return sign;
+    int e;
+    (void)frexp(a, &e);
+    int E = e - 1;
+    int qexp = (E >= -126) ? E - 7 : -133; /* exponent of one bf16 ulp at a */
+    double scaled = ldexp(a, -qexp);
+    double fl = floor(scaled);
+    double frac = scaled - fl;
+    uint64_t n = (uint64_t)fl;
+    if (frac > 0.5 || (frac == 0.5 && (n & 1)))
+        n += 1;
+    if (E >= -126) {
+        /* normal binade: n in [128, 256] */
+        if (n == 256) {
+            n = 128;
+            qexp += 1;
+        }
+        int biased = qexp + 7 + 127;
+        if (biased >= 255)
+            return (uint16_t)(sign | 0x7f80);
+        return (uint16_t)(sign | (biased << 7) | (uint16_t)(n - 128));
+    }
+    /* subnormal range: n in [0, 128]; 128 is the smallest normal, 0x0080 */
+    return (uint16_t)(sign | n);
+}
+
+void oracle_bf16_to_double_array(const uint16_t *h, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_to_double(h[i]);
+}
+
+void oracle_double_to_bf16_array(const double *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_double_to_bf16(x[i]);
+}
+
 void oracle_half_to_double_array(const uint16_t *h, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
@@ -104,6 +179,7 @@ struct job {
     int64_t nrows;
     int64_t r_begin, r_end;
     const double *lut;
+    uint16_t (*encode)(double);
 };
 
 static void *run_rows(void *p)
@@ -123,7 +199,7 @@ static void *run_rows(void *p)
             }
             int64_t o = r * jb->N + j;
             if (jb->D)
-                jb->D[o] = oracle_double_to_half(s);
+                jb->D[o] = jb->encode(s);
             if (jb->sum)
                 jb->sum[o] = s;
             if (jb->bound)
@@ -141,11 +217,10 @@ static void *run_rows(void *p)
  * taken in increasing k, so results do not depend on the thread count.
  * Returns 0, or -1 on invalid arguments.
  */
-int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
-                    double *bound, double *sum,
-                    int64_t M, int64_t N, int64_t K,
-                    int64_t lda, int64_t ldb,
-                    const int64_t *rows, int64_t nrows, int nthreads)
+static int gemm16(const uint16_t *A, const uint16_t *B, uint16_t *D, double *bound,
+                  double *sum, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                  const int64_t *rows, int64_t nrows, int nthreads,
+                  double (*decode)(uint16_t), uint16_t (*encode)(double))
 {
     if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || nrows < 0)
         return -1;
@@ -162,7 +237,7 @@ int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
     if (!lut)
         return -1;
     for (uint32_t h = 0; h < 65536; ++h)
-        lut[h] = oracle_half_to_double((uint16_t)h);
+        lut[h] = decode((uint16_t)h);
 
     if (nthreads < 1)
         nthreads = 1;
@@ -180,7 +255,7 @@ int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
     for (int t = 0; t < nthreads; ++t) {
         int64_t cnt = per + (t < extra ? 1 : 0);
         struct job jb = {A, B, D, bound, sum, N, K, lda, ldb, rows, nrows,
-                         start, start + cnt, lut};
+                         start, start + cnt, lut, encode};
         jobs[t] = jb;
         start += cnt;
     }
@@ -200,4 +275,25 @@ int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
     free(th);
     free(jobs);
     return 0;
+}
+
+int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
+                    double *bound, double *sum,
+                    int64_t M, int64_t N, int64_t K,
+                    int64_t lda, int64_t ldb,
+                    const int64_t *rows, int64_t nrows, int nthreads)
+{
+    return gemm16(A, B, D, bound, sum, M, N, K, lda, ldb, rows, nrows, nthreads,
+                  oracle_half_to_double, oracle_double_to_half);
+}
+
+/* The same GEMM on bfloat16 operands and output (products exact in fp64). */
+int oracle_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *D,
+                     double *bound, double *sum,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb,
+                     const int64_t *rows, int64_t nrows, int nthreads)
+{
+    return gemm16(A, B, D, bound, sum, M, N, K, lda, ldb, rows, nrows, nthreads,
+                  oracle_bf16_to_double, oracle_double_to_bf16);
 }

@@ -13,6 +13,11 @@ with round-to-nearest-even (numpy's ``astype(np.float16)``).
 Reading of "N(0, 1/K)": the second parameter is the variance, so the weights
 have standard deviation 1/sqrt(K).  "N(0,1)/4" is a standard normal divided
 by four.
+
+bfloat16 operands (for the bf16 entry point) are returned as uint16 bit
+patterns: the same float64 draws, cast to float32 by numpy and cut to their
+upper 16 bits (truncation: these are simply the inputs, not a rounding of
+anything the GEMM computes).
 """
 from __future__ import annotations
 
@@ -63,19 +68,30 @@ WORKLOADS = [
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
-def _draw(rng: np.random.Generator, shape, dist) -> np.ndarray:
+def _draw64(rng: np.random.Generator, shape, dist) -> np.ndarray:
     kind = dist[0]
     if kind == "uniform":
-        x = rng.uniform(dist[1], dist[2], size=shape)
-    elif kind == "normal":
-        x = rng.standard_normal(size=shape) * dist[2] + dist[1]
-    else:
-        raise ValueError(f"unknown distribution {dist!r}")
-    return x.astype(np.float16)
+        return rng.uniform(dist[1], dist[2], size=shape)
+    if kind == "normal":
+        return rng.standard_normal(size=shape) * dist[2] + dist[1]
+    raise ValueError(f"unknown distribution {dist!r}")
 
 
-def make_inputs(w: Workload, lda: Optional[int] = None, ldb: Optional[int] = None):
-    """Return (A, B) as float16 arrays of shape (M, lda) and (N, ldb).
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 draws → bfloat16 bit patterns (float32 cast, low half cut)."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _draw(rng: np.random.Generator, shape, dist, dtype: str = "f16") -> np.ndarray:
+    x = _draw64(rng, shape, dist)
+    return to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float16)
+
+
+def make_inputs(w: Workload, lda: Optional[int] = None, ldb: Optional[int] = None,
+                dtype: str = "f16"):
+    """Return (A, B) of shape (M, lda) and (N, ldb): float16 arrays, or
+    uint16 bfloat16 bit patterns with ``dtype="bf16"``.
 
     The logical operands are A[:, :K] and B[:, :K]; padding columns (when
     lda > K or ldb > K) are filled with NaN so that any read past K shows up
@@ -83,8 +99,8 @@ def make_inputs(w: Workload, lda: Optional[int] = None, ldb: Optional[int] = Non
     """
     lda = w.K if lda is None else lda
     ldb = w.K if ldb is None else ldb
-    a = _draw(np.random.Generator(np.random.PCG64(SEED_A_BASE + w.index)), (w.M, w.K), w.dist_a)
-    b = _draw(np.random.Generator(np.random.PCG64(SEED_B_BASE + w.index)), (w.N, w.K), w.dist_b)
+    a = _draw(np.random.Generator(np.random.PCG64(SEED_A_BASE + w.index)), (w.M, w.K), w.dist_a, dtype)
+    b = _draw(np.random.Generator(np.random.PCG64(SEED_B_BASE + w.index)), (w.N, w.K), w.dist_b, dtype)
     if lda != w.K:
         a = pad_columns(a, lda)
     if ldb != w.K:
@@ -92,12 +108,19 @@ def make_inputs(w: Workload, lda: Optional[int] = None, ldb: Optional[int] = Non
     return a, b
 
 
+BF16_NAN = np.uint16(0x7fc0)
+
+
 def pad_columns(x: np.ndarray, ld: int, fill=np.nan) -> np.ndarray:
-    """Copy a (rows, K) fp16 matrix into a (rows, ld) buffer, padding with ``fill``."""
+    """Copy a (rows, K) matrix into a (rows, ld) buffer, padding with ``fill``
+    (NaN; for uint16 bf16 bit arrays the bf16 NaN pattern)."""
     rows, k = x.shape
     if ld < k:
         raise ValueError("leading dimension smaller than the row length")
-    out = np.full((rows, ld), fill, dtype=np.float16)
+    if x.dtype == np.uint16:
+        out = np.full((rows, ld), BF16_NAN if np.isnan(fill) else fill, dtype=np.uint16)
+    else:
+        out = np.full((rows, ld), fill, dtype=np.float16)
     out[:, :k] = x
     return out
 
@@ -116,6 +139,11 @@ def random_f16(seed: int, shape, dist=("normal", 0.0, 1.0)) -> np.ndarray:
     return _draw(np.random.Generator(np.random.PCG64(seed)), shape, dist)
 
 
+def random_bf16(seed: int, shape, dist=("normal", 0.0, 1.0)) -> np.ndarray:
+    """Seeded bfloat16 operands as uint16 bit patterns."""
+    return _draw(np.random.Generator(np.random.PCG64(seed)), shape, dist, "bf16")
+
+
 def index_pattern(M: int, N: int, K: int):
     """Integer-valued operands whose products are exact in fp32 and fp16 for
     K <= 341: A[i,k] = ((i + 2k) mod 5) - 2 and B[j,k] = ((3j + k) mod 7) - 3,
@@ -126,3 +154,17 @@ def index_pattern(M: int, N: int, K: int):
     a = (((i + 2 * k) % 5) - 2).astype(np.float16)
     b = (((3 * j + k) % 7) - 3).astype(np.float16)
     return a, b
+
+
+def small_int_pattern(M: int, N: int, K: int, dtype: str = "f16"):
+    """Operands in {-1, 0, 1}: A[i,k] = ((i + 2k) mod 3) - 1, B[j,k] =
+    ((2j + k) mod 3) - 1, so |D| <= K and D is exact in bfloat16 for K <= 256
+    (and in binary16 for K <= 2048)."""
+    i = np.arange(M)[:, None]
+    j = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    a = (((i + 2 * k) % 3) - 1).astype(np.float64)
+    b = (((2 * j + k) % 3) - 1).astype(np.float64)
+    if dtype == "bf16":
+        return to_bf16_bits(a), to_bf16_bits(b)
+    return a.astype(np.float16), b.astype(np.float16)
