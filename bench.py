@@ -131,7 +131,8 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = False):
+def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = False,
+                  dtype: str = "f16"):
     import numpy as np
     import torch
 
@@ -139,17 +140,20 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
     import workloads
 
     dev = torch.device("cuda:0")
-    a, b = workloads.make_inputs(w)
-    A0 = torch.from_numpy(a).to(dev)
-    B0 = torch.from_numpy(b).to(dev)
+    a, b = workloads.make_inputs(w, dtype=dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    A0 = torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
+    B0 = torch.from_numpy(b.view(np.int16)).to(dev).view(tdt)
     sets = []
     for r in range(rotate):
         A = A0 if r == 0 else A0.clone()
         B = B0 if r == 0 else B0.clone()
-        D = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+        D = torch.empty((w.M, w.N), dtype=tdt, device=dev)
         sets.append((A, B, D))
     stream = torch.cuda.current_stream(dev)
-    st, kname, tiles = tg.tg_gemm_f16_plan(A0, B0, sets[0][2], w.M, w.N, w.K, w.K, w.K, w.N)
+    plan = tg.tg_gemm_bf16_plan if dtype == "bf16" else tg.tg_gemm_f16_plan
+    call = tg.tg_gemm_bf16 if dtype == "bf16" else tg.tg_gemm_f16
+    st, kname, tiles = plan(A0, B0, sets[0][2], w.M, w.N, w.K, w.K, w.K, w.N)
     if st != tg.TG_OK:
         raise RuntimeError(tg.tg_status_string(st))
 
@@ -158,9 +162,9 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
         if vendor:  # context only: the vendor library on the same inputs
             torch.matmul(A, B.t(), out=D)
             return
-        s = tg.tg_gemm_f16(A, B, D, w.M, w.N, w.K, w.K, w.K, w.N, stream)
+        s = call(A, B, D, w.M, w.N, w.K, w.K, w.K, w.N, stream)
         if s != tg.TG_OK:
-            raise RuntimeError(f"tg_gemm_f16: {tg.tg_status_string(s)}")
+            raise RuntimeError(f"{call.__name__}: {tg.tg_status_string(s)}")
 
     for i in range(warmup):
         step(i)
@@ -180,7 +184,7 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
     return dict(ms=ms, wall_s=wall, kernel=kname, tiles=tiles, a=a, b=b)
 
 
-def cpu_baseline(w, a, b, seconds: float, rows_override=None):
+def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16"):
     """Time the oracle on the first R rows of D (all N columns, full K)."""
     import numpy as np
 
@@ -192,13 +196,13 @@ def cpu_baseline(w, a, b, seconds: float, rows_override=None):
     else:
         probe = min(max(1, threads), w.M)
         t0 = time.perf_counter()
-        oracle.gemm(a, b, w.M, w.N, w.K, rows=np.arange(probe), nthreads=threads)
+        oracle.gemm(a, b, w.M, w.N, w.K, rows=np.arange(probe), nthreads=threads, fmt=fmt)
         per_row = (time.perf_counter() - t0) / probe
         R = int(min(w.M, max(threads, seconds / max(per_row, 1e-9))))
         R = max(threads, (R // threads) * threads) if R >= threads else R
     rows = np.arange(R, dtype=np.int64)
     t0 = time.perf_counter()
-    oracle.gemm(a, b, w.M, w.N, w.K, rows=rows, nthreads=threads)
+    oracle.gemm(a, b, w.M, w.N, w.K, rows=rows, nthreads=threads, fmt=fmt)
     t = time.perf_counter() - t0
     flop = 2.0 * R * w.N * w.K
     return {
@@ -223,6 +227,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and print a table on stderr")
+    ap.add_argument("--dtype", choices=["f16", "bf16"], default="f16",
+                    help="element type (the headline metric is fp16; bf16 is reported alongside)")
     ap.add_argument("--vendor", action="store_true",
                     help="with --all: also time torch.matmul on the same inputs (context)")
     ap.add_argument("--copy-bytes", type=int, default=None,
@@ -259,18 +265,18 @@ def main() -> int:
     if args.all:
         log(f"{'workload':28s} {'kernel':32s} {'us':>9s} {'TFLOP/s':>9s} {'%peak':>7s} {'GB/s':>8s}")
         for ww in workloads.WORKLOADS:
-            r = time_workload(ww, args.steps, args.warmup)
+            r = time_workload(ww, args.steps, args.warmup, dtype=args.dtype)
             tf = ww.flop / (r["ms"] * 1e-3) / 1e12
             gbs = ww.min_bytes / (r["ms"] * 1e-3) / 1e9
             log(f"{ww.name:28s} {r['kernel']:32s} {r['ms'] * 1e3:9.2f} {tf:9.1f} "
                 f"{100 * tf / PEAK_FP16_TFLOPS:7.2f} {gbs:8.0f}")
             if args.vendor:
-                v = time_workload(ww, args.steps, args.warmup, vendor=True)
+                v = time_workload(ww, args.steps, args.warmup, vendor=True, dtype=args.dtype)
                 tfv = ww.flop / (v["ms"] * 1e-3) / 1e12
                 log(f"{'':28s} {'torch.matmul':32s} {v['ms'] * 1e3:9.2f} {tfv:9.1f} "
                     f"{100 * tfv / PEAK_FP16_TFLOPS:7.2f} {ww.min_bytes / (v['ms'] * 1e-3) / 1e9:8.0f}")
 
-    r = time_workload(w, args.steps, args.warmup)
+    r = time_workload(w, args.steps, args.warmup, dtype=args.dtype)
     ms = r["ms"]
     tflops = w.flop / (ms * 1e-3) / 1e12
     log(f"{w.name}: {r['kernel']} tiles={r['tiles']} {ms * 1e3:.2f} us/launch "
@@ -278,12 +284,14 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, r["a"], r["b"], args.cpu_seconds, args.cpu_rows)
+        cpu = cpu_baseline(w, r["a"], r["b"], args.cpu_seconds, args.cpu_rows, args.dtype)
         log(f"cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
     traffic = measured_traffic(r["kernel"], w.name)
     line = {
-        "metric": "TFLOP/s fp16 GEMM D=A·B^T at 8192x14336x4096; % of MFMA dense fp16 peak",
+        "metric": ("TFLOP/s fp16 GEMM D=A·B^T at 8192x14336x4096; % of MFMA dense fp16 peak"
+                   if args.dtype == "f16" else
+                   "TFLOP/s bf16 GEMM D=A·B^T at 8192x14336x4096; % of MFMA dense bf16 peak"),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -293,7 +301,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "kernel": r["kernel"],
                    "tiles": r["tiles"], "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2)},

@@ -1,4 +1,4 @@
-"""Python binding of libtg_gemm.so — the MI355X (gfx950) fp16 GEMM D = A·Bᵀ.
+"""Python binding of libtg_gemm.so — the MI355X (gfx950) fp16/bf16 GEMM D = A·Bᵀ.
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``csrc/tg_gemm.hip``.  There is no fallback: if the library is
@@ -6,8 +6,9 @@ not built, importing the functions below raises.
 
     tg_gemm_f16(A, B, D, M, N, K, lda, ldb, ldd, stream) -> status
     tg_gemm_f16_plan(A, B, D, M, N, K, lda, ldb, ldd) -> (status, name, tiles)
+    tg_gemm_bf16(...), tg_gemm_bf16_plan(...)   the same for bfloat16 data
     tg_status_string(status) -> str
-    gemm(A, B, out=None, stream=None) -> D   (torch convenience wrapper)
+    gemm(A, B, out=None, stream=None) -> D   (torch wrapper; fp16 or bf16)
 
 Pointers may be given as torch tensors (their ``data_ptr()``) or integers;
 ``stream`` may be a ``torch.cuda.Stream``, an integer hipStream_t or None
@@ -19,8 +20,8 @@ import ctypes
 import os
 
 __all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_ERR_TOO_LARGE",
-           "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_status_string",
-           "gemm"]
+           "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_gemm_bf16",
+           "tg_gemm_bf16_plan", "tg_status_string", "gemm"]
 
 TG_OK = 0
 TG_ERR_INVALID_ARG = -1
@@ -55,11 +56,13 @@ def load():
     lib = ctypes.CDLL(_LIB_PATH)
     i64 = ctypes.c_int64
     vp = ctypes.c_void_p
-    lib.tg_gemm_f16.restype = ctypes.c_int
-    lib.tg_gemm_f16.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
-    lib.tg_gemm_f16_plan.restype = ctypes.c_int
-    lib.tg_gemm_f16_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64,
-                                     ctypes.c_char_p, i64, ctypes.POINTER(i64)]
+    for fn in (lib.tg_gemm_f16, lib.tg_gemm_bf16):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    for fn in (lib.tg_gemm_f16_plan, lib.tg_gemm_bf16_plan):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                       ctypes.c_char_p, i64, ctypes.POINTER(i64)]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -97,18 +100,35 @@ def tg_gemm_f16_plan(A, B, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: i
     return st, buf.value.decode(), tiles.value
 
 
+def tg_gemm_bf16(A, B, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int, stream=None) -> int:
+    """Enqueue D ← bf16_rne(A·Bᵀ) on ``stream`` (bfloat16 data); returns the C status code."""
+    return load().tg_gemm_bf16(_ptr(A), _ptr(B), _ptr(D), M, N, K, lda, ldb, ldd, _stream(stream))
+
+
+def tg_gemm_bf16_plan(A, B, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int):
+    """Host-only: (status, kernel name, output tile count) for tg_gemm_bf16."""
+    buf = ctypes.create_string_buffer(128)
+    tiles = ctypes.c_int64(0)
+    st = load().tg_gemm_bf16_plan(_ptr(A), _ptr(B), _ptr(D), M, N, K, lda, ldb, ldd, buf, 128,
+                                  ctypes.byref(tiles))
+    return st, buf.value.decode(), tiles.value
+
+
 def tg_status_string(status: int) -> str:
     return load().tg_status_string(status).decode()
 
 
 def gemm(A, B, out=None, stream=None):
-    """torch convenience: D = A·Bᵀ for fp16 CUDA tensors A (M×K) and B (N×K)
-    whose last dimension is contiguous.  Uses torch's current stream when
-    ``stream`` is None.  Raises TgError on a non-zero status."""
+    """torch convenience: D = A·Bᵀ for fp16 or bf16 CUDA tensors A (M×K) and
+    B (N×K) of the same dtype whose last dimension is contiguous; D has that
+    dtype.  Uses torch's current stream when ``stream`` is None.  Raises
+    TgError on a non-zero status."""
     import torch
 
-    if A.dtype != torch.float16 or B.dtype != torch.float16:
-        raise TypeError("A and B must be float16")
+    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("A and B must both be float16 or both bfloat16")
+    dt = A.dtype
+    call = tg_gemm_f16 if dt == torch.float16 else tg_gemm_bf16
     if A.dim() != 2 or B.dim() != 2 or A.stride(1) != 1 or B.stride(1) != 1:
         raise ValueError("A and B must be 2-D with a contiguous last dimension")
     M, K = A.shape
@@ -116,15 +136,15 @@ def gemm(A, B, out=None, stream=None):
     if K2 != K:
         raise ValueError(f"K mismatch: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
-    elif out.dtype != torch.float16 or out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
-        raise ValueError("out must be a float16 (M, N) tensor with a contiguous last dimension")
+        out = torch.empty((M, N), dtype=dt, device=A.device)
+    elif out.dtype != dt or out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
+        raise ValueError(f"out must be a {dt} (M, N) tensor with a contiguous last dimension")
     if stream is None:
         stream = torch.cuda.current_stream(A.device)
     lda = A.stride(0) if M > 1 else max(K, 1)
     ldb = B.stride(0) if N > 1 else max(K, 1)
     ldd = out.stride(0) if M > 1 else max(N, 1)
-    st = tg_gemm_f16(A, B, out, M, N, K, max(lda, K), max(ldb, K), max(ldd, N), stream)
+    st = call(A, B, out, M, N, K, max(lda, K), max(ldb, K), max(ldd, N), stream)
     if st != TG_OK:
-        raise TgError(st)
+        raise TgError(st, call.__name__)
     return out

@@ -30,9 +30,34 @@
 
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Element type of A, B and D: binary16 or bfloat16.  Both take the same
+// tiles, DMAs and LDS layouts (2-byte elements); they differ only in the
+// MFMA that consumes the fragments and in the fp32 → element conversion of
+// the epilogue (a C cast: round to nearest even for both).
+template <typename E>
+struct Elem;
+template <>
+struct Elem<_Float16> {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+    static constexpr const char *prefix = "gemm_f16_";
+    __device__ static f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Elem<__bf16> {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+    static constexpr const char *prefix = "gemm_bf16_";
+    __device__ static f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
 
 __host__ __device__ constexpr int imin(int a, int b) { return a < b ? a : b; }
 
@@ -129,8 +154,8 @@ static_assert(tile_order_is_bijective(32, 56) && tile_order_is_bijective(16, 16)
 // One 16-byte chunk (8 consecutive K) of row `row` of a K-major operand,
 // zero outside rows [0,rows) or K.  VEC: 16-byte aligned rows with K % 8 == 0,
 // so a chunk is either wholly inside K or wholly outside.
-template <bool VEC>
-__device__ inline uint4 load_chunk(const _Float16 *__restrict__ base, int64_t ld, int row,
+template <bool VEC, typename E>
+__device__ inline uint4 load_chunk(const E *__restrict__ base, int64_t ld, int row,
                                    int rows, int k, int K)
 {
     if constexpr (VEC) {
@@ -141,11 +166,11 @@ __device__ inline uint4 load_chunk(const _Float16 *__restrict__ base, int64_t ld
     } else {
         union {
             uint4 u;
-            _Float16 h[8];
+            E h[8];
         } v;
         v.u = make_uint4(0, 0, 0, 0);
         if (row < rows) {
-            const _Float16 *p = base + (int64_t)row * ld;
+            const E *p = base + (int64_t)row * ld;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (k + e < K)
@@ -159,12 +184,14 @@ __device__ inline uint4 load_chunk(const _Float16 *__restrict__ base, int64_t ld
 // of D built from 32×32 MFMA tiles.  The MFMA "A" input is fed from B and
 // the MFMA "B" input from A, so each lane's accumulator holds four
 // consecutive columns of one row of D (see the store loop).
-template <int BM, int BN, int WM, int WN, bool VEC>
-__global__ __launch_bounds__(WM *WN * 64) void gemm_f16_kernel(
-    const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
+template <typename E, int BM, int BN, int WM, int WN, bool VEC>
+__global__ __launch_bounds__(WM *WN * 64) void gemm_vec_kernel(
+    const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
     int dvec)
 {
+    using V8 = typename Elem<E>::v8;
+    using V4 = typename Elem<E>::v4;
     constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -176,7 +203,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_f16_kernel(
     constexpr int STAGE = (BM + BN) * BK;
     static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(1024))) _Float16 smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) E smem[2 * STAGE];
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -189,8 +216,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_f16_kernel(
     // global → LDS assignment: thread loads chunk (tid & 7) of rows
     // (tid >> 3) + p·RS, p = 0..PASSES-1
     const int lrow = tid >> 3, lch = tid & 7;
-    const _Float16 *a_base = A + (int64_t)m0 * lda;
-    const _Float16 *b_base = B + (int64_t)n0 * ldb;
+    const E *a_base = A + (int64_t)m0 * lda;
+    const E *b_base = B + (int64_t)n0 * ldb;
     const int a_rows = M - m0, b_rows = N - n0;
     const int st_off = lds_chunk_off(lrow, lch);
 
@@ -205,8 +232,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_f16_kernel(
             rb[p] = load_chunk<VEC>(b_base, ldb, lrow + p * RS, b_rows, k, K);
     };
     auto lstore = [&](int s) {
-        _Float16 *as = smem + s * STAGE;
-        _Float16 *bs = as + BM * BK;
+        E *as = smem + s * STAGE;
+        E *bs = as + BM * BK;
 #pragma unroll
         for (int p = 0; p < A_PASSES; ++p)
             *reinterpret_cast<uint4 *>(as + st_off + p * RS * BK) = ra[p];
@@ -238,25 +265,25 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_f16_kernel(
         const int s = kt & 1;
         if (kt + 1 < KT)
             gload(kt + 1);
-        const _Float16 *as = smem + s * STAGE;
-        const _Float16 *bs = as + BM * BK;
+        const E *as = smem + s * STAGE;
+        const E *bs = as + BM * BK;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const int c = kk * 2 + frag_hi;
-            f16x8 af[TM], bf[TN];
+            V8 af[TM], bf[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const f16x8 *>(
+                af[i] = *reinterpret_cast<const V8 *>(
                     as + lds_chunk_off(wm * WTM + i * 32 + frag_row, c));
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bf[j] = *reinterpret_cast<const f16x8 *>(
+                bf[j] = *reinterpret_cast<const V8 *>(
                     bs + lds_chunk_off(wn * WTN + j * 32 + frag_row, c));
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = Elem<E>::mfma(bf[j], af[i], acc[i][j]);
         }
         if (kt + 1 < KT)
             lstore(s ^ 1);
@@ -271,18 +298,18 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_f16_kernel(
         const int row = m0 + wm * WTM + i * 32 + frag_row;
         if (row >= M)
             continue;
-        _Float16 *drow = D + (int64_t)row * ldd;
+        E *drow = D + (int64_t)row * ldd;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int col = n0 + wn * WTN + j * 32 + g * 8 + frag_hi * 4;
-                f16x4 h;
+                V4 h;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[r] = (_Float16)acc[i][j][g * 4 + r];  // v_cvt_f16_f32: round to nearest even
+                    h[r] = (E)acc[i][j][g * 4 + r];  // v_cvt_f16_f32: round to nearest even
                 if (dvec && col + 3 < N) {
-                    *reinterpret_cast<f16x4 *>(drow + col) = h;
+                    *reinterpret_cast<V4 *>(drow + col) = h;
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -327,7 +354,7 @@ constexpr uint32_t DMA_OOB = 0x80000000u;
 // in the device pass; the host pass sees an empty body, which keeps clang
 // emitting the host-side kernel stubs.
 template <int CPOL = 0>
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, _Float16 *lds, uint32_t voff)
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, void *lds, uint32_t voff)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)lds, 16, voff, 0, 0, CPOL);
@@ -419,12 +446,14 @@ static_assert(tg::layout::check_swizzled_tile(tg::layout::swizzle_bank256_f16(25
 //   0 is read and the drained stage is refilled with K-tile kt+STAGES (past
 //   the end: an all-out-of-range DMA, i.e. a no-op that keeps the loop
 //   branch-free and the vmcnt bookkeeping uniform).
-template <int BM, int BN, int WM, int WN, int BK_, int STAGES, int OCC, int DMA_STEPS, int KROT>
-__global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? WM * WN / 4 : 1)) void gemm_f16_dma_kernel(
-    const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
+template <typename E, int BM, int BN, int WM, int WN, int BK_, int STAGES, int OCC, int DMA_STEPS, int KROT>
+__global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? WM * WN / 4 : 1)) void gemm_dma_kernel(
+    const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
     int dvec)
 {
+    using V8 = typename Elem<E>::v8;
+    using V4 = typename Elem<E>::v4;
     using T = OperandTile<BK_>;
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -443,7 +472,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
     constexpr int VM_IN_FLIGHT = (STAGES - 2) * DMA_PER_TILE;
     static_assert((STAGES - 1) * DMA_PER_TILE <= 63, "vmcnt holds 6 bits");
 
-    __shared__ __attribute__((aligned(1024))) _Float16 smem[STAGES * STAGE];
+    __shared__ __attribute__((aligned(1024))) E smem[STAGES * STAGE];
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -477,7 +506,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
 
     struct DmaTile {
         __amdgpu_buffer_rsrc_t ra, rb;
-        _Float16 *as, *bs;
+        E *as, *bs;
         int klim;  // valid K elements in this K-tile (0 past the end)
     };
     // K-tile order: this workgroup starts at K-tile krot and wraps around.
@@ -515,17 +544,17 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
     };
 
     const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
-    f16x8 fa[2][TM], fb[2][TN];
+    V8 fa[2][TM], fb[2][TN];
     // one fragment of K-step kk of the K-tile in stage s: q < TM is A
     // fragment q, else B fragment q - TM
-    auto read_frag = [&](int s, int kk, int q, f16x8 *a, f16x8 *b) {
-        const _Float16 *as = smem + s * STAGE;
-        const _Float16 *bs = as + BM * BK_;
+    auto read_frag = [&](int s, int kk, int q, V8 *a, V8 *b) {
+        const E *as = smem + s * STAGE;
+        const E *bs = as + BM * BK_;
         const int c = kk * 2 + frag_hi;
         if (q < TM)
-            a[q] = *reinterpret_cast<const f16x8 *>(as + T::off(wm * WTM + q * 32 + frag_row, c));
+            a[q] = *reinterpret_cast<const V8 *>(as + T::off(wm * WTM + q * 32 + frag_row, c));
         else
-            b[q - TM] = *reinterpret_cast<const f16x8 *>(
+            b[q - TM] = *reinterpret_cast<const V8 *>(
                 bs + T::off(wn * WTN + (q - TM) * 32 + frag_row, c));
     };
 
@@ -552,13 +581,13 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
     // `every` slots, so they spread evenly over the step (between and beside
     // the fragment reads) instead of arriving at the memory pipe in a burst;
     // passes that outnumber the slots go after the last MFMA.
-    auto step = [&](const f16x8 *a, const f16x8 *b, bool with_reads, int rs, int rkk, f16x8 *na,
-                    f16x8 *nb, const DmaTile *dma, int lo, int hi, int every) {
+    auto step = [&](const V8 *a, const V8 *b, bool with_reads, int rs, int rkk, V8 *na,
+                    V8 *nb, const DmaTile *dma, int lo, int hi, int every) {
         constexpr int first = 1;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const int ti = i / TN, tj = i % TN;
-            acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[tj], a[ti], acc[ti][tj], 0, 0, 0);
+            acc[ti][tj] = Elem<E>::mfma(b[tj], a[ti], acc[ti][tj]);
             MFMA_FIRST();
             if (with_reads && i < NFRAG)
                 read_frag(rs, rkk, frag_of_slot(i), na, nb);
@@ -656,20 +685,20 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
     static_assert((SCH & (SCH - 1)) == 0 && SCH >= 2, "chunk swizzle needs a power of two");
     auto stage_off = [](int r, int chunk) { return r * SROW + ((chunk ^ (r & (SCH - 1))) << 3); };
     barrier_lds();
-    _Float16 *stg = smem + wave * WTM * WTN;
+    E *stg = smem + wave * WTM * WTN;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                f16x4 h;
+                V4 h;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[r] = (_Float16)acc[i][j][g * 4 + r];  // round to nearest even
+                    h[r] = (E)acc[i][j][g * 4 + r];  // round to nearest even
                 const int r = i * 32 + frag_row;
                 const int c = j * 32 + g * 8 + frag_hi * 4;
-                *reinterpret_cast<f16x4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
+                *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
             }
     // read back: lane l takes chunk l mod SCH of row l / SCH (+ 64/SCH rows per pass)
     constexpr int ROWS_PER_PASS = 64 / SCH;
@@ -678,12 +707,12 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
 #pragma unroll
     for (int pass = 0; pass < WTM / ROWS_PER_PASS; ++pass) {
         const int r = pass * ROWS_PER_PASS + rr;
-        const f16x8 v = *reinterpret_cast<const f16x8 *>(stg + stage_off(r, rc));
+        const V8 v = *reinterpret_cast<const V8 *>(stg + stage_off(r, rc));
         const int row = m0 + wm * WTM + r;
         if (row < M) {
-            _Float16 *dst = D + (int64_t)row * ldd + col;
+            E *dst = D + (int64_t)row * ldd + col;
             if (dvec && col + 7 < N) {
-                *reinterpret_cast<f16x8 *>(dst) = v;
+                *reinterpret_cast<V8 *>(dst) = v;
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -694,7 +723,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
     }
 }
 
-// Variant of gemm_f16_dma_kernel for the largest tile with separate LDS rings
+// Variant of gemm_dma_kernel for the largest tile with separate LDS rings
 // for the two operands: three stages of A and two of B (BK = 64: 3·32 + 2·32
 // KiB = 160 KiB for 256×256).  With one ring of two stages the refill of a
 // drained stage has one K-tile to land, so its 16 DMAs per wave had to be
@@ -709,13 +738,15 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
 //   barrier (A stage t mod 3 and B stage t mod 2 are drained)
 //   K-step 3: B(t+2), first half (and the fragments of K-tile t+1, step 0)
 // Everything else (swizzle, fragment reads, tails, staged epilogue) is as in
-// gemm_f16_dma_kernel; rows past M or N are clamped.
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma3_kernel(
-    const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
+// gemm_dma_kernel; rows past M or N are clamped.
+template <typename E, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_kernel(
+    const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
     int dvec)
 {
+    using V8 = typename Elem<E>::v8;
+    using V4 = typename Elem<E>::v4;
     constexpr int BK_ = 64, SA = 3, SB = 2;
     using T = OperandTile<BK_>;
     constexpr int NW = WM * WN;
@@ -732,9 +763,9 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
     static_assert((SA * STAGE_A + SB * STAGE_B) * 2 <= 160 * 1024, "LDS budget");
     static_assert(A_PASSES + BH + A_PASSES <= 63, "vmcnt holds 6 bits");
 
-    __shared__ __attribute__((aligned(1024))) _Float16 smem[SA * STAGE_A + SB * STAGE_B];
-    _Float16 *const a_ring = smem;
-    _Float16 *const b_ring = smem + SA * STAGE_A;
+    __shared__ __attribute__((aligned(1024))) E smem[SA * STAGE_A + SB * STAGE_B];
+    E *const a_ring = smem;
+    E *const b_ring = smem + SA * STAGE_A;
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -766,7 +797,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
     // DMA source and LDS stage of one operand's K-tile
     struct Op {
         __amdgpu_buffer_rsrc_t r;
-        _Float16 *dst;
+        E *dst;
         int klim;  // valid K elements (0 past the end)
     };
     auto op_a = [&](int t) {
@@ -797,15 +828,15 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
     };
 
     const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
-    f16x8 fa[2][TM], fb[2][TN];
+    V8 fa[2][TM], fb[2][TN];
     // fragment q of K-step kk of the K-tile in A stage sa / B stage sb
-    auto read_frag = [&](int sa, int sb, int kk, int q, f16x8 *a, f16x8 *b) {
+    auto read_frag = [&](int sa, int sb, int kk, int q, V8 *a, V8 *b) {
         const int c = kk * 2 + frag_hi;
         if (q < TM)
-            a[q] = *reinterpret_cast<const f16x8 *>(a_ring + sa * STAGE_A +
+            a[q] = *reinterpret_cast<const V8 *>(a_ring + sa * STAGE_A +
                                                     T::off(wm * WTM + q * 32 + frag_row, c));
         else
-            b[q - TM] = *reinterpret_cast<const f16x8 *>(
+            b[q - TM] = *reinterpret_cast<const V8 *>(
                 b_ring + sb * STAGE_B + T::off(wn * WTN + (q - TM) * 32 + frag_row, c));
     };
 
@@ -827,14 +858,14 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
     // One K-step: MFMA per slot; the next step's read i after MFMA i (i <
     // NFRAG); the DMA passes [lo, hi) of `o` (A when is_a) from slot 1 at an
     // even stride; passes that outnumber the slots go after the last MFMA.
-    auto step = [&](const f16x8 *a, const f16x8 *b, bool with_reads, int rsa, int rsb, int rkk,
-                    f16x8 *na, f16x8 *nb, const Op *o, bool is_a, int lo, int hi) {
+    auto step = [&](const V8 *a, const V8 *b, bool with_reads, int rsa, int rsb, int rkk,
+                    V8 *na, V8 *nb, const Op *o, bool is_a, int lo, int hi) {
         const int n = hi - lo;
         const int every = n > 0 && SLOTS / n > 0 ? SLOTS / n : 1;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const int ti = i / TN, tj = i % TN;
-            acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[tj], a[ti], acc[ti][tj], 0, 0, 0);
+            acc[ti][tj] = Elem<E>::mfma(b[tj], a[ti], acc[ti][tj]);
             MFMA_FIRST();
             if (with_reads && i % RSTRIDE == 0 && i / RSTRIDE < NFRAG)
                 read_frag(rsa, rsb, rkk, frag_of_slot(i / RSTRIDE), na, nb);
@@ -903,27 +934,27 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
     }
     wait_vmem<0>();  // no LDS DMA may be outstanding when the wave ends
 
-    // staged epilogue, as in gemm_f16_dma_kernel
+    // staged epilogue, as in gemm_dma_kernel
     static_assert(NW * WTM * WTN <= SA * STAGE_A + SB * STAGE_B, "staging fits in the stage memory");
     constexpr int SROW = WTN;
     constexpr int SCH = WTN / 8;
     static_assert((SCH & (SCH - 1)) == 0 && SCH >= 2, "chunk swizzle needs a power of two");
     auto stage_off = [](int r, int chunk) { return r * SROW + ((chunk ^ (r & (SCH - 1))) << 3); };
     barrier_lds();
-    _Float16 *stg = smem + wave * WTM * WTN;
+    E *stg = smem + wave * WTM * WTN;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                f16x4 h;
+                V4 h;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[r] = (_Float16)acc[i][j][g * 4 + r];  // round to nearest even
+                    h[r] = (E)acc[i][j][g * 4 + r];  // round to nearest even
                 const int r = i * 32 + frag_row;
                 const int c = j * 32 + g * 8 + frag_hi * 4;
-                *reinterpret_cast<f16x4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
+                *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
             }
     constexpr int ROWS_PER_PASS = 64 / SCH;
     const int rc = lane % SCH, rr = lane / SCH;
@@ -931,12 +962,12 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
 #pragma unroll
     for (int pass = 0; pass < WTM / ROWS_PER_PASS; ++pass) {
         const int r = pass * ROWS_PER_PASS + rr;
-        const f16x8 v = *reinterpret_cast<const f16x8 *>(stg + stage_off(r, rc));
+        const V8 v = *reinterpret_cast<const V8 *>(stg + stage_off(r, rc));
         const int row = m0 + wm * WTM + r;
         if (row < M) {
-            _Float16 *dst = D + (int64_t)row * ldd + col;
+            E *dst = D + (int64_t)row * ldd + col;
             if (dvec && col + 7 < N) {
-                *reinterpret_cast<f16x8 *>(dst) = v;
+                *reinterpret_cast<V8 *>(dst) = v;
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -949,14 +980,14 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_f16_dma
 
 struct KernelChoice {
     const void *fn;
-    const char *name;
+    const char *tile;  // "<BM>x<BN>_w<WM>x<WN>"
     int bm, bn, threads;
     int path;
 };
 
 // Compile-time tuning of the direct-to-LDS kernels: K-tile depth (BK), LDS
 // ring depth (STAGES) and DMA spread per workgroup tile size (M: 128×128,
-// S: 64×64, K*: column strips; the 256×256 tile uses gemm_f16_dma3_kernel).
+// S: 64×64, K*: column strips; the 256×256 tile uses gemm_dma3_kernel).
 // The defaults are the measured best on MI355X.
 #ifndef TG_M_DMA_STEPS
 #define TG_M_DMA_STEPS 1
@@ -987,27 +1018,23 @@ struct KernelChoice {
 // (aligned operands whose in-tile offsets exceed 32 bits), or element-wise.
 enum LoadPath { PATH_DMA = 0, PATH_VEC = 1, PATH_SCALAR = 2 };
 
-template <int BM, int BN, int WM, int WN, int DMA_BK, int DMA_STAGES, int DMA_STEPS = 1,
-          int OCC = 1, int KROT = 0>
-KernelChoice choice(LoadPath path, const char *const names[3])
+template <typename E, int BM, int BN, int WM, int WN, int DMA_BK, int DMA_STAGES,
+          int DMA_STEPS = 1, int OCC = 1, int KROT = 0>
+KernelChoice choice(LoadPath path, const char *tile)
 {
-    const void *fn = path == PATH_DMA
-                         ? reinterpret_cast<const void *>(
-                               &gemm_f16_dma_kernel<BM, BN, WM, WN, DMA_BK, DMA_STAGES, OCC, DMA_STEPS, KROT>)
-                     : path == PATH_VEC
-                         ? reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, true>)
-                         : reinterpret_cast<const void *>(&gemm_f16_kernel<BM, BN, WM, WN, false>);
-    return {fn, names[path], BM, BN, WM * WN * 64, path};
+    const void *fn =
+        path == PATH_DMA
+            ? reinterpret_cast<const void *>(
+                  &gemm_dma_kernel<E, BM, BN, WM, WN, DMA_BK, DMA_STAGES, OCC, DMA_STEPS, KROT>)
+        : path == PATH_VEC ? reinterpret_cast<const void *>(&gemm_vec_kernel<E, BM, BN, WM, WN, true>)
+                           : reinterpret_cast<const void *>(&gemm_vec_kernel<E, BM, BN, WM, WN, false>);
+    return {fn, tile, BM, BN, WM * WN * 64, path};
 }
 
-constexpr const char *NAMES_256[3] = {"gemm_f16_256x256_w2x2_dma", "gemm_f16_256x256_w2x2_vec",
-                                      "gemm_f16_256x256_w2x2_scalar"};
+constexpr const char *PATH_SUFFIX[3] = {"_dma", "_vec", "_scalar"};
 #define TG_STR2(x) #x
 #define TG_STR(x) TG_STR2(x)
-#define TG_NAMES(bm, bn, wm, wn)                                                              \
-    {"gemm_f16_" TG_STR(bm) "x" TG_STR(bn) "_w" TG_STR(wm) "x" TG_STR(wn) "_dma",             \
-     "gemm_f16_" TG_STR(bm) "x" TG_STR(bn) "_w" TG_STR(wm) "x" TG_STR(wn) "_vec",             \
-     "gemm_f16_" TG_STR(bm) "x" TG_STR(bn) "_w" TG_STR(wm) "x" TG_STR(wn) "_scalar"}
+#define TG_TILE(bm, bn, wm, wn) TG_STR(bm) "x" TG_STR(bn) "_w" TG_STR(wm) "x" TG_STR(wn)
 // Column-strip tiles for small M: one tile row covers all of M.
 #ifndef TG_K_BN
 #define TG_K_BN 128
@@ -1045,13 +1072,12 @@ constexpr const char *NAMES_256[3] = {"gemm_f16_256x256_w2x2_dma", "gemm_f16_256
 #ifndef TG_K_MAXM
 #define TG_K_MAXM 256
 #endif
-constexpr const char *NAMES_STRIP64[3] = TG_NAMES(64, TG_K_BN, 1, TG_K_WN);
-constexpr const char *NAMES_STRIP128[3] = TG_NAMES(128, 128, TG_K2_WM, 4 / TG_K2_WM);
-constexpr const char *NAMES_STRIP256[3] = TG_NAMES(256, 128, 2, 2);
-constexpr const char *NAMES_128[3] = {"gemm_f16_128x128_w2x2_dma", "gemm_f16_128x128_w2x2_vec",
-                                      "gemm_f16_128x128_w2x2_scalar"};
-constexpr const char *NAMES_64[3] = {"gemm_f16_64x64_w2x2_dma", "gemm_f16_64x64_w2x2_vec",
-                                     "gemm_f16_64x64_w2x2_scalar"};
+constexpr const char *TILE_STRIP64 = TG_TILE(64, TG_K_BN, 1, TG_K_WN);
+constexpr const char *TILE_STRIP128 = TG_TILE(128, 128, TG_K2_WM, 4 / TG_K2_WM);
+constexpr const char *TILE_STRIP256 = TG_TILE(256, 128, 2, 2);
+constexpr const char *TILE_256 = TG_TILE(256, 256, 2, 2);
+constexpr const char *TILE_128 = TG_TILE(128, 128, 2, 2);
+constexpr const char *TILE_64 = TG_TILE(64, 64, 2, 2);
 
 constexpr int64_t LIMIT32 = (int64_t)1 << 31;
 constexpr int NUM_CU = 256;
@@ -1076,6 +1102,7 @@ struct Plan {
     int dvec;
 };
 
+template <typename E>
 Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N, int64_t K,
                int64_t lda, int64_t ldb, int64_t ldd)
 {
@@ -1091,26 +1118,28 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     // Small M, large N (HBM-bound streaming of B): one tile row covers all of
     // M, so B is read exactly once, and the XCDs start at spread K offsets.
     if (TG_K_ON && M <= 64 && tiles(64, TG_K_BN) >= NUM_CU / 2)
-        k = choice<64, TG_K_BN, 1, TG_K_WN, TG_K_BK, TG_K_STAGES, TG_K_DS, 1, 1>(path(64, TG_K_BN),
-                                                                                  NAMES_STRIP64);
+        k = choice<E, 64, TG_K_BN, 1, TG_K_WN, TG_K_BK, TG_K_STAGES, TG_K_DS, 1, 1>(
+            path(64, TG_K_BN), TILE_STRIP64);
     else if (TG_K_ON && M <= 128 && TG_K_MAXM >= 128 && tiles(128, 128) >= NUM_CU / 2)
-        k = choice<128, 128, TG_K2_WM, 4 / TG_K2_WM, TG_K2_BK, TG_K2_STAGES, 2, 1, 1>(path(128, 128),
-                                                                                       NAMES_STRIP128);
+        k = choice<E, 128, 128, TG_K2_WM, 4 / TG_K2_WM, TG_K2_BK, TG_K2_STAGES, 2, 1, 1>(
+            path(128, 128), TILE_STRIP128);
     else if (TG_K_ON && M <= 256 && TG_K_MAXM >= 256 && tiles(256, 128) >= NUM_CU / 2)
-        k = choice<256, 128, 2, 2, TG_K4_BK, TG_K4_STAGES, 2, 1, 1>(path(256, 128), NAMES_STRIP256);
+        k = choice<E, 256, 128, 2, 2, TG_K4_BK, TG_K4_STAGES, 2, 1, 1>(path(256, 128), TILE_STRIP256);
     else
     if (tiles(256, 256) >= NUM_CU) {
         const LoadPath lp = path(256, 256);
         if (lp == PATH_DMA)
-            k = {reinterpret_cast<const void *>(&gemm_f16_dma3_kernel<256, 256, 2, 2>),
-                 NAMES_256[PATH_DMA], 256, 256, 256, PATH_DMA};
+            k = {reinterpret_cast<const void *>(&gemm_dma3_kernel<E, 256, 256, 2, 2>), TILE_256, 256,
+                 256, 256, PATH_DMA};
         else
-            k = choice<256, 256, 2, 2, 64, 2>(lp, NAMES_256);
+            k = choice<E, 256, 256, 2, 2, 64, 2>(lp, TILE_256);
     }
     else if (tiles(128, 128) >= NUM_CU)
-        k = choice<128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT>(path(128, 128), NAMES_128);
+        k = choice<E, 128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT>(path(128, 128),
+                                                                                       TILE_128);
     else
-        k = choice<64, 64, 2, 2, TG_S_BK, TG_S_STAGES, TG_S_DMA_STEPS, 1, TG_S_KROT>(path(64, 64), NAMES_64);
+        k = choice<E, 64, 64, 2, 2, TG_S_BK, TG_S_STAGES, TG_S_DMA_STEPS, 1, TG_S_KROT>(path(64, 64),
+                                                                                     TILE_64);
     Plan p;
     p.k = k;
     p.tiles_m = (int)((M + k.bm - 1) / k.bm);
@@ -1143,10 +1172,9 @@ int check_device()
     return ok ? TG_OK : TG_ERR_DEVICE;
 }
 
-}  // namespace
-
-extern "C" int tg_gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N,
-                           int64_t K, int64_t lda, int64_t ldb, int64_t ldd, void *stream)
+template <typename E>
+int launch(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, int64_t lda,
+           int64_t ldb, int64_t ldd, void *stream)
 {
     int st = validate(A, B, D, M, N, K, lda, ldb, ldd);
     if (st != TG_OK)
@@ -1156,7 +1184,7 @@ extern "C" int tg_gemm_f16(const void *A, const void *B, void *D, int64_t M, int
     st = check_device();
     if (st != TG_OK)
         return st;
-    Plan p = make_plan(A, B, D, M, N, K, lda, ldb, ldd);
+    Plan p = make_plan<E>(A, B, D, M, N, K, lda, ldb, ldd);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
     if (grid >= LIMIT32)
         return TG_ERR_TOO_LARGE;
@@ -1168,9 +1196,9 @@ extern "C" int tg_gemm_f16(const void *A, const void *B, void *D, int64_t M, int
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
-extern "C" int tg_gemm_f16_plan(const void *A, const void *B, const void *D, int64_t M,
-                                int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
-                                char *name, int64_t name_len, int64_t *tiles)
+template <typename E>
+int plan(const void *A, const void *B, const void *D, int64_t M, int64_t N, int64_t K,
+         int64_t lda, int64_t ldb, int64_t ldd, char *name, int64_t name_len, int64_t *tiles)
 {
     int st = validate(A, B, D, M, N, K, lda, ldb, ldd);
     if (name && name_len > 0)
@@ -1179,12 +1207,40 @@ extern "C" int tg_gemm_f16_plan(const void *A, const void *B, const void *D, int
         *tiles = 0;
     if (st != TG_OK || M == 0 || N == 0)
         return st;
-    Plan p = make_plan(A, B, D, M, N, K, lda, ldb, ldd);
+    Plan p = make_plan<E>(A, B, D, M, N, K, lda, ldb, ldd);
     if (name && name_len > 0)
-        snprintf(name, (size_t)name_len, "%s", p.k.name);
+        snprintf(name, (size_t)name_len, "%s%s%s", Elem<E>::prefix, p.k.tile, PATH_SUFFIX[p.k.path]);
     if (tiles)
         *tiles = (int64_t)p.tiles_m * p.tiles_n;
     return TG_OK;
+}
+
+}  // namespace
+
+extern "C" int tg_gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N,
+                           int64_t K, int64_t lda, int64_t ldb, int64_t ldd, void *stream)
+{
+    return launch<_Float16>(A, B, D, M, N, K, lda, ldb, ldd, stream);
+}
+
+extern "C" int tg_gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N,
+                            int64_t K, int64_t lda, int64_t ldb, int64_t ldd, void *stream)
+{
+    return launch<__bf16>(A, B, D, M, N, K, lda, ldb, ldd, stream);
+}
+
+extern "C" int tg_gemm_f16_plan(const void *A, const void *B, const void *D, int64_t M,
+                                int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
+                                char *name, int64_t name_len, int64_t *tiles)
+{
+    return plan<_Float16>(A, B, D, M, N, K, lda, ldb, ldd, name, name_len, tiles);
+}
+
+extern "C" int tg_gemm_bf16_plan(const void *A, const void *B, const void *D, int64_t M,
+                                 int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
+                                 char *name, int64_t name_len, int64_t *tiles)
+{
+    return plan<__bf16>(A, B, D, M, N, K, lda, ldb, ldd, name, name_len, tiles);
 }
 
 extern "C" const char *tg_status_string(int status)

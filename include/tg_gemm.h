@@ -87,6 +87,28 @@ int tg_gemm_f16_plan(const void *A, const void *B, const void *D,
                      int64_t lda, int64_t ldb, int64_t ldd,
                      char *name, int64_t name_len, int64_t *tiles);
 
+/*
+ * tg_gemm_bf16 — the same operation on bfloat16 data: D = A·Bᵀ with A, B and
+ * D bfloat16 (bit patterns in 2-byte elements, same layout, strides, edge
+ * cases, streams, threading and return codes as tg_gemm_f16), products
+ * accumulated in fp32 and the result rounded to bfloat16 to nearest even.
+ * "从编译器能力到公开算子", section "SM90a 支持具体补了什么": the matrix
+ * path takes FP16 or BF16 inputs with FP32 accumulation; the pages name no
+ * BF16 output rounding, and round-to-nearest-even (the fp16 epilogue's
+ * cvt.rn) is the reading taken.
+ */
+int tg_gemm_bf16(const void *A, const void *B, void *D,
+                 int64_t M, int64_t N, int64_t K,
+                 int64_t lda, int64_t ldb, int64_t ldd,
+                 void *stream);
+
+/* tg_gemm_bf16_plan — tg_gemm_f16_plan for tg_gemm_bf16 (names start with
+ * "gemm_bf16_"). */
+int tg_gemm_bf16_plan(const void *A, const void *B, const void *D,
+                      int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldd,
+                      char *name, int64_t name_len, int64_t *tiles);
+
 /* tg_status_string — a static, NUL-terminated description of a status. */
 const char *tg_status_string(int status);
 

@@ -15,27 +15,33 @@ def say(msg: str) -> None:
     print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
 
 
-def to_dev(x: np.ndarray, offset_elems: int = 0):
-    """Copy a 2-D fp16 array into a device buffer starting `offset_elems`
-    elements past a 256-byte aligned allocation (offset 1 misaligns it)."""
+NAN_BITS = {"f16": 0x7e00, "bf16": 0x7fc0}
+
+
+def to_dev(x: np.ndarray, offset_elems: int = 0, fmt: str = "f16"):
+    """Copy a 2-D 16-bit array (fp16 values, or bf16 bit patterns as uint16)
+    into a device buffer starting `offset_elems` elements past a 256-byte
+    aligned allocation (offset 1 misaligns it); the rest of the buffer holds
+    NaN of that format."""
     import torch
 
-    flat = np.ascontiguousarray(x, dtype=np.float16).reshape(-1)
-    buf = torch.empty(flat.size + offset_elems + 8, dtype=torch.float16, device="cuda:0")
-    buf.fill_(float("nan"))
-    if flat.size:
-        buf[offset_elems:offset_elems + flat.size].copy_(torch.from_numpy(flat))
+    raw = np.ascontiguousarray(x).reshape(-1).view(np.uint16).view(np.int16)
+    buf = torch.full((raw.size + offset_elems + 8,), NAN_BITS[fmt], dtype=torch.int16,
+                     device="cuda:0")
+    if raw.size:
+        buf[offset_elems:offset_elems + raw.size].copy_(torch.from_numpy(raw))
     return buf, buf.data_ptr() + 2 * offset_elems
 
 
 def run(a: np.ndarray, b: np.ndarray, M: int, N: int, K: int, *, ldd: int | None = None,
         guard: int = 0, a_off: int = 0, b_off: int = 0, d_off: int = 0, stream=None,
-        label: str = ""):
-    """D = A·Bᵀ on the GPU.  a is (M, lda) and b is (N, ldb) fp16 (padding
-    columns beyond K are passed through untouched).  D lives in a buffer of
-    (M + 2·guard) rows × ldd_total columns filled with SENTINEL, with the
-    window at (guard, guard).  Returns (D window as fp16 (M, N), full buffer
-    as uint16 for guard checks, status)."""
+        label: str = "", fmt: str = "f16"):
+    """D = A·Bᵀ on the GPU.  a is (M, lda) and b is (N, ldb) fp16, or bf16 bit
+    patterns (uint16) with fmt="bf16" (padding columns beyond K are passed
+    through untouched).  D lives in a buffer of (M + 2·guard) rows ×
+    ldd_total columns filled with SENTINEL, with the window at (guard,
+    guard).  Returns (D window as fp16 (M, N) — uint16 bits for bf16 — full
+    buffer as uint16 for guard checks, status)."""
     import torch
 
     import dense_fp16_gemm_02_amd as tg
@@ -44,19 +50,22 @@ def run(a: np.ndarray, b: np.ndarray, M: int, N: int, K: int, *, ldd: int | None
     ldb = b.shape[1] if b.ndim == 2 and b.shape[1] else max(K, 1)
     ldd = (N + 2 * guard) if ldd is None else ldd
     rows_total = M + 2 * guard
-    a_buf, a_ptr = to_dev(a, a_off)
-    b_buf, b_ptr = to_dev(b, b_off)
+    a_buf, a_ptr = to_dev(a, a_off, fmt)
+    b_buf, b_ptr = to_dev(b, b_off, fmt)
     d_buf = torch.full((rows_total * ldd + d_off + 8,), 0, dtype=torch.int16, device="cuda:0")
     d_buf.fill_(SENTINEL)
     d_ptr = d_buf.data_ptr() + 2 * (d_off + guard * ldd + guard)
     s = stream if stream is not None else torch.cuda.current_stream()
-    say(f"{label} M={M} N={N} K={K} lda={lda} ldb={ldb} ldd={ldd} guard={guard} "
+    say(f"{label} {fmt} M={M} N={N} K={K} lda={lda} ldb={ldb} ldd={ldd} guard={guard} "
         f"offs=({a_off},{b_off},{d_off})")
-    st = tg.tg_gemm_f16(a_ptr, b_ptr, d_ptr, M, N, K, lda, ldb, ldd, s)
+    call = tg.tg_gemm_bf16 if fmt == "bf16" else tg.tg_gemm_f16
+    st = call(a_ptr, b_ptr, d_ptr, M, N, K, lda, ldb, ldd, s)
     s.synchronize()
     torch.cuda.synchronize()
     full = d_buf.cpu().numpy().view(np.uint16)[d_off:d_off + rows_total * ldd].reshape(rows_total, ldd)
-    win = full[guard:guard + M, guard:guard + N].view(np.float16)
+    win = full[guard:guard + M, guard:guard + N]
+    if fmt != "bf16":
+        win = win.view(np.float16)
     del a_buf, b_buf
     return np.array(win), full, st
 

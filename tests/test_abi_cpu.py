@@ -119,3 +119,14 @@ def test_binding_refuses_without_library(tmp_path, monkeypatch):
     with pytest.raises(ImportError):
         pkg.load()
     importlib.reload(pkg)
+
+
+def test_bf16_plans_and_validation():
+    for w in workloads.WORKLOADS:
+        st, name, tiles = tg.tg_gemm_bf16_plan(FAKE, FAKE, FAKE, w.M, w.N, w.K, w.K, w.K, w.N)
+        st16, name16, tiles16 = tg.tg_gemm_f16_plan(FAKE, FAKE, FAKE, w.M, w.N, w.K, w.K, w.K, w.N)
+        assert st == tg.TG_OK and name == name16.replace("gemm_f16_", "gemm_bf16_")
+        assert tiles == tiles16
+    assert tg.tg_gemm_bf16(FAKE, FAKE, FAKE, 4, 4, 8, 4, 8, 4, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_bf16(FAKE, FAKE, FAKE, 1 << 31, 4, 4, 4, 4, 4, None) == tg.TG_ERR_TOO_LARGE
+    assert tg.tg_gemm_bf16(None, None, None, 0, 0, 0, 0, 0, 0, None) == tg.TG_OK

@@ -1,0 +1,184 @@
+"""GPU parity of tg_gemm_bf16 (through the C ABI) against the CPU oracle's
+bfloat16 GEMM on the same seeded inputs.
+
+Acceptance per checked element: |D − ref| ≤ 4e-3·Σ|a||b| + ulp_bf16(ref), D
+finite.  The same kernels serve both element types (only the MFMA and the
+epilogue conversion differ), so these tests cover the paths the bf16 entry
+point takes: the workloads (small ones on every element, the large ones on
+sampled rows), exact integer operands through every tile family, the
+rounding of the epilogue, tails, strides, alignment and K = 0."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import guard_intact, run, say
+
+torch = pytest.importorskip("torch")
+tg = pytest.importorskip("dense_fp16_gemm_02_amd")
+
+pytestmark = pytest.mark.gpu
+
+FAKE = 1 << 20
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tg.load()
+    torch.cuda.init()
+
+
+def _check(d, res, what):
+    ok, worst, report = oracle.check(d, res)
+    assert ok, f"{what}: {report}"
+
+
+def _dev(x: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_workload_every_element(idx):
+    w = workloads.WORKLOADS[idx]
+    a, b = workloads.make_inputs(w, dtype="bf16")
+    d, full, st = run(a, b, w.M, w.N, w.K, guard=8, label=w.name, fmt="bf16")
+    assert st == tg.TG_OK and guard_intact(full, w.M, w.N, 8)
+    _check(d, oracle.gemm(a, b, w.M, w.N, w.K, fmt="bf16"), w.name)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_workload_sampled_rows(idx):
+    w = workloads.WORKLOADS[idx]
+    a, b = workloads.make_inputs(w, dtype="bf16")
+    say(f"bf16 {w.name}: upload")
+    A, B = _dev(a), _dev(b)
+    D = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda:0")
+    say(f"bf16 {w.name}: launch")
+    st = tg.tg_gemm_bf16(A, B, D, w.M, w.N, w.K, w.K, w.K, w.N, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == tg.TG_OK
+    rows = workloads.sample_rows(w)
+    d = D[torch.from_numpy(rows).to("cuda:0")].view(torch.int16).cpu().numpy().view(np.uint16)
+    _check(d, oracle.gemm(a, b, w.M, w.N, w.K, rows=rows, fmt="bf16"), w.name)
+    assert bool(torch.isfinite(D.float()).all())
+
+
+@pytest.mark.parametrize("M,N,K,tile", [
+    (128, 128, 64, "64x64"), (1000, 1000, 200, "64x64"), (257, 263, 136, "64x64"),
+    (2100, 2000, 256, "128x128"), (4352 - 5, 4352 - 3, 136, "256x256"),
+    (64, 16411, 200, "64x128"), (100, 16390, 256, "128x128"), (200, 16500, 136, "256x128"),
+])
+def test_small_int_pattern_exact(M, N, K, tile):
+    """Operands in {-1, 0, 1} with K <= 256: D is exact in bf16, so every
+    checked element must equal the integer product; one shape per tile."""
+    a, b = workloads.small_int_pattern(M, N, K, "bf16")
+    st0, name, tiles = tg.tg_gemm_bf16_plan(FAKE, FAKE, FAKE, M, N, K, K, K, N + 2)
+    say(f"bf16 plan {name} tiles={tiles}")
+    assert st0 == tg.TG_OK and name.startswith(f"gemm_bf16_{tile}_") and name.endswith("_dma")
+    d, full, st = run(a, b, M, N, K, guard=1, label="bf16 small-int", fmt="bf16")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 1)
+    rows = np.unique(np.concatenate([np.arange(0, min(M, 160)), np.arange(max(0, M - 160), M)]))
+    ai = oracle.bf16_to_double(a[rows]).astype(np.int64)
+    bi = oracle.bf16_to_double(b).astype(np.int64)
+    assert np.array_equal(oracle.bf16_to_double(d[rows]).astype(np.int64), ai @ bi.T)
+
+
+def test_rounding_is_nearest_even():
+    """Rows whose fp32 sums are exact and sit on or next to bfloat16 rounding
+    points; only the epilogue's conversion decides."""
+    rows = [
+        [1.0, 2.0 ** -8],                      # tie → 1.0 (even)
+        [1.0, 2.0 ** -7, 2.0 ** -8],           # tie → 1 + 2^-6 (even)
+        [1.0, 2.0 ** -8, 2.0 ** -9],           # above the tie → 1 + 2^-7
+        [1.0, 2.0 ** -8, -(2.0 ** -10)],       # below the tie → 1.0
+        [-1.0, -(2.0 ** -8), -(2.0 ** -9)],    # negative, above the tie → away from 0
+        [256.0, 1.0],                          # tie at ulp 2 → 256
+        [256.0, 1.0, 2.0],                     # 259 → 260
+        [2.0 ** 127 * 1.9921875, 2.0 ** 119],  # largest finite + half ulp → +inf
+        [2.0 ** 127 * 1.9921875, 2.0 ** 118],  # stays at the largest finite
+    ]
+    K = 64
+    a = np.zeros((len(rows), K), dtype=np.uint16)
+    for i, r in enumerate(rows):
+        a[i, :len(r)] = workloads.to_bf16_bits(np.array(r))
+    b = np.full((32, K), 0x3f80, dtype=np.uint16)
+    d, _, st = run(a, b, len(rows), 32, K, label="bf16 rounding", fmt="bf16")
+    assert st == tg.TG_OK
+    res = oracle.gemm(a, b, len(rows), 32, K, fmt="bf16")
+    assert np.array_equal(d, res.d)
+    assert [int(x) for x in d[:, 0]] == [0x3f80, 0x3f82, 0x3f81, 0x3f80, 0xbf81, 0x4380,
+                                         0x4382, 0x7f80, 0x7f7f]
+
+
+@pytest.mark.parametrize("case", [
+    dict(M=200, N=136, K=96, lda=104, ldb=120, ldd=150),
+    dict(M=77, N=301, K=40, lda=48, ldb=40, ldd=304),
+])
+def test_padded_strides_with_nan_poison(case):
+    M, N, K = case["M"], case["N"], case["K"]
+    a0 = workloads.random_bf16(131, (M, K))
+    b0 = workloads.random_bf16(132, (N, K))
+    a = workloads.pad_columns(a0, case["lda"])
+    b = workloads.pad_columns(b0, case["ldb"])
+    d, full, st = run(a, b, M, N, K, ldd=case["ldd"], label="bf16 padded", fmt="bf16")
+    assert st == tg.TG_OK
+    _check(d, oracle.gemm(a0, b0, M, N, K, fmt="bf16"), "bf16 padded")
+
+
+@pytest.mark.parametrize("offs", [(1, 0, 0), (0, 3, 0), (0, 0, 1)])
+def test_misaligned_pointers(offs):
+    M, N, K = 150, 190, 136
+    a = workloads.random_bf16(141, (M, K))
+    b = workloads.random_bf16(142, (N, K))
+    d, full, st = run(a, b, M, N, K, guard=2, a_off=offs[0], b_off=offs[1], d_off=offs[2],
+                      label="bf16 misaligned", fmt="bf16")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 2)
+    _check(d, oracle.gemm(a, b, M, N, K, fmt="bf16"), "bf16 misaligned")
+
+
+@pytest.mark.parametrize("K", [1, 7, 65, 1001])
+def test_k_not_multiple_of_8(K):
+    M, N = 97, 131
+    a = workloads.random_bf16(150 + K, (M, K))
+    b = workloads.random_bf16(160 + K, (N, K))
+    d, full, st = run(a, b, M, N, K, guard=1, label="bf16 odd-K", fmt="bf16")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 1)
+    _check(d, oracle.gemm(a, b, M, N, K, fmt="bf16"), f"bf16 K={K}")
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (65, 129), (257, 511), (4100, 4200)])
+def test_ragged_tails(M, N):
+    K = 200 if M < 4096 else 1000
+    a = workloads.random_bf16(170 + M, (M, K))
+    b = workloads.random_bf16(180 + N, (N, K))
+    d, full, st = run(a, b, M, N, K, guard=2, label="bf16 tails", fmt="bf16")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 2)
+    if M < 4096:
+        _check(d, oracle.gemm(a, b, M, N, K, fmt="bf16"), f"bf16 {M}x{N}")
+    else:
+        rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(M - 260, M)]))
+        _check(d[rows], oracle.gemm(a, b, M, N, K, rows=rows, fmt="bf16"), f"bf16 {M}x{N}")
+
+
+def test_zero_k_gives_positive_zero():
+    M, N = 70, 90
+    a = np.full((M, 8), 0x7fc0, dtype=np.uint16)   # never read
+    b = np.full((N, 8), 0x7fc0, dtype=np.uint16)
+    d, full, st = run(a, b, M, N, 0, guard=2, label="bf16 K=0", fmt="bf16")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 2)
+    assert np.all(d == 0)
+
+
+def test_torch_wrapper_matches():
+    A = torch.randn(333, 256, device="cuda:0").to(torch.bfloat16)
+    B = torch.randn(444, 256, device="cuda:0").to(torch.bfloat16)
+    say("bf16 torch wrapper")
+    D = tg.gemm(A, B)
+    torch.cuda.synchronize()
+    assert D.dtype == torch.bfloat16
+    a = A.view(torch.int16).cpu().numpy().view(np.uint16)
+    b = B.view(torch.int16).cpu().numpy().view(np.uint16)
+    d = D.view(torch.int16).cpu().numpy().view(np.uint16)
+    _check(d, oracle.gemm(a, b, 333, 444, 256, fmt="bf16"), "bf16 wrapper")
