@@ -74,8 +74,8 @@ def traffic_record(args) -> int:
     gf, gw, cf, cw = args.traffic_record
     copy_bytes = args.copy_bytes
     kernel, workload = args.traffic_kernel, args.workload
-    g_fetch, n1 = _pmc_per_dispatch(gf, "FETCH_SIZE", "gemm_f16")
-    g_write, n2 = _pmc_per_dispatch(gw, "WRITE_SIZE", "gemm_f16")
+    g_fetch, n1 = _pmc_per_dispatch(gf, "FETCH_SIZE", "gemm_")
+    g_write, n2 = _pmc_per_dispatch(gw, "WRITE_SIZE", "gemm_")
     c_fetch, _ = _pmc_per_dispatch(cf, "FETCH_SIZE", "copyBuffer")
     c_write, _ = _pmc_per_dispatch(cw, "WRITE_SIZE", "copyBuffer")
     k_fetch = copy_bytes / c_fetch  # bytes per counter unit (nominally 1024: KiB)
