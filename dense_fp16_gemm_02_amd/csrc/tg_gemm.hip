@@ -415,6 +415,61 @@ static_assert(tg::layout::check_swizzled_tile(tg::layout::swizzle_bank256_f16(25
                                               OperandTile<32>::off),
               "BK=32 LDS addressing disagrees with ComposeLayout(3, 2, 4)");
 
+// Second half of the staged epilogue: one wave's WTM×WTN block of D, held
+// in LDS as row-major fp16 with the 16-byte chunk index of row r XORed with
+// r mod (WTN/8) (stage_off), goes to global memory 16 bytes per lane along
+// rows: lane l takes chunk l mod (WTN/8) of row l / (WTN/8), 512/WTN rows per
+// pass, so each store instruction writes 64·16 bytes as whole row segments.
+// A block wholly inside D with 16-byte aligned rows (dvec) issues its LDS
+// reads in batches ahead of the stores, with no per-row branches; a block
+// on an edge checks every row against M and every column against N.
+template <typename E, int WTM, int WTN, typename SO>
+__device__ inline void store_staged_block(const E *stg, SO stage_off, E *__restrict__ D, int64_t ldd,
+                                          int row0, int col0, int M, int N, int dvec, int lane)
+{
+    using V8 = typename Elem<E>::v8;
+    constexpr int SCH = WTN / 8;
+    constexpr int ROWS_PER_PASS = 64 / SCH;
+    constexpr int PASSES = WTM / ROWS_PER_PASS;
+    static_assert(WTM % ROWS_PER_PASS == 0, "whole passes");
+    const int rc = lane % SCH, rr = lane / SCH;
+    const int col = col0 + 8 * rc;
+    if (dvec && row0 + WTM <= M && col0 + WTN <= N) {
+        constexpr int BATCH = PASSES < 16 ? PASSES : 16;
+        static_assert(PASSES % BATCH == 0, "whole batches");
+        E *dst = D + (int64_t)(row0 + rr) * ldd + col;
+        const int64_t pass_stride = (int64_t)ROWS_PER_PASS * ldd;
+#pragma unroll
+        for (int p0 = 0; p0 < PASSES; p0 += BATCH) {
+            V8 v[BATCH];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+                v[b] = *reinterpret_cast<const V8 *>(stg + stage_off((p0 + b) * ROWS_PER_PASS + rr, rc));
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+                *reinterpret_cast<V8 *>(dst + (p0 + b) * pass_stride) = v[b];
+        }
+        return;
+    }
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+        const int r = pass * ROWS_PER_PASS + rr;
+        const V8 v = *reinterpret_cast<const V8 *>(stg + stage_off(r, rc));
+        const int row = row0 + r;
+        if (row < M) {
+            E *dst = D + (int64_t)row * ldd + col;
+            if (dvec && col + 7 < N) {
+                *reinterpret_cast<V8 *>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < N)
+                        dst[e] = v[e];
+            }
+        }
+    }
+}
+
 // Main path for 16-byte aligned operands with K, lda, ldb multiples of 8 and
 // in-tile byte offsets below 2^31 (see dma_offsets_fit).
 //
@@ -700,27 +755,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
                 const int c = j * 32 + g * 8 + frag_hi * 4;
                 *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
             }
-    // read back: lane l takes chunk l mod SCH of row l / SCH (+ 64/SCH rows per pass)
-    constexpr int ROWS_PER_PASS = 64 / SCH;
-    const int rc = lane % SCH, rr = lane / SCH;
-    const int col = n0 + wn * WTN + 8 * rc;
-#pragma unroll
-    for (int pass = 0; pass < WTM / ROWS_PER_PASS; ++pass) {
-        const int r = pass * ROWS_PER_PASS + rr;
-        const V8 v = *reinterpret_cast<const V8 *>(stg + stage_off(r, rc));
-        const int row = m0 + wm * WTM + r;
-        if (row < M) {
-            E *dst = D + (int64_t)row * ldd + col;
-            if (dvec && col + 7 < N) {
-                *reinterpret_cast<V8 *>(dst) = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (col + e < N)
-                        dst[e] = v[e];
-            }
-        }
-    }
+    store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
 }
 
 // Variant of gemm_dma_kernel for the largest tile with separate LDS rings
@@ -956,26 +991,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
                 const int c = j * 32 + g * 8 + frag_hi * 4;
                 *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
             }
-    constexpr int ROWS_PER_PASS = 64 / SCH;
-    const int rc = lane % SCH, rr = lane / SCH;
-    const int col = n0 + wn * WTN + 8 * rc;
-#pragma unroll
-    for (int pass = 0; pass < WTM / ROWS_PER_PASS; ++pass) {
-        const int r = pass * ROWS_PER_PASS + rr;
-        const V8 v = *reinterpret_cast<const V8 *>(stg + stage_off(r, rc));
-        const int row = m0 + wm * WTM + r;
-        if (row < M) {
-            E *dst = D + (int64_t)row * ldd + col;
-            if (dvec && col + 7 < N) {
-                *reinterpret_cast<V8 *>(dst) = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (col + e < N)
-                        dst[e] = v[e];
-            }
-        }
-    }
+    store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
 }
 
 struct KernelChoice {
