@@ -1,4 +1,5 @@
-"""CPU oracle for the fp16 (and bf16) GEMM D = A·Bᵀ — test infrastructure only.
+"""CPU oracle for the fp16 (and bf16, and block-scaled FP8) GEMM D = A·Bᵀ —
+test infrastructure only.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg may import this package.  The GPU library never does,
@@ -15,6 +16,10 @@ the output term is ulp_bf16(ref) = 2^(⌊log2|x|⌋−7) (2^−133 below 2^−12
 
 bfloat16 arrays are passed and returned as uint16 bit patterns (numpy has no
 bfloat16 type); ``fmt="bf16"`` selects that format everywhere.
+
+``gemm_mx`` is the block-scaled FP8 GEMM: E4M3 operand bytes, one UE8M0 scale
+byte per 32 K elements of each row, fp16 output; its bound is
+Σ_k |sa·a|·|sb·b| and the acceptance check is the fp16 one.
 """
 from __future__ import annotations
 
@@ -67,6 +72,13 @@ def _load():
     lib.oracle_bf16_to_double_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
     lib.oracle_double_to_bf16_array.restype = None
     lib.oracle_double_to_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+    lib.oracle_e4m3_to_double_array.restype = None
+    lib.oracle_e4m3_to_double_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+    lib.oracle_e8m0_to_double.restype = ctypes.c_double
+    lib.oracle_e8m0_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_gemm_mxf8.restype = ctypes.c_int
+    lib.oracle_gemm_mxf8.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 7 + [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
     for fn in (lib.oracle_gemm_f16, lib.oracle_gemm_bf16):
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
@@ -112,6 +124,21 @@ def double_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.uint16)
     _load().oracle_double_to_bf16_array(x.ctypes.data, out.ctypes.data, x.size)
     return out
+
+
+def e4m3_to_double(b: np.ndarray) -> np.ndarray:
+    """Exact FP8 E4M3 (uint8 codes) → float64 decode (NaN for 0x7f, 0xff)."""
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_e4m3_to_double_array(b.ctypes.data, out.ctypes.data, b.size)
+    return out
+
+
+def e8m0_to_double(s: np.ndarray) -> np.ndarray:
+    """UE8M0 scale bytes → float64 powers of two (NaN for 255)."""
+    s = np.asarray(s, dtype=np.uint8)
+    f = _load().oracle_e8m0_to_double
+    return np.vectorize(lambda v: f(int(v)), otypes=[np.float64])(s) if s.size else np.zeros(s.shape)
 
 
 def decode(x: np.ndarray, fmt: str) -> np.ndarray:
@@ -177,6 +204,43 @@ def gemm(a: np.ndarray, b: np.ndarray, M: int, N: int, K: int,
         raise ValueError("oracle rejected its arguments")
     out_rows = np.arange(M, dtype=np.int64) if rows is None else rows_arr
     return Result(d, bound, total, out_rows, fmt)
+
+
+def gemm_mx(a: np.ndarray, sa: np.ndarray, b: np.ndarray, sb: np.ndarray, M: int, N: int, K: int,
+            rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None) -> Result:
+    """Reference block-scaled FP8 GEMM on uint8 arrays: ``a`` (M×lda E4M3
+    codes), ``sa`` (M×ldsa UE8M0 scale bytes, one per 32 K elements), and
+    likewise ``b``, ``sb`` for the N rows of B.  Returns fp16 D for the
+    requested rows with the float64 sum and bound beside it."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.uint8)
+    sb = np.ascontiguousarray(sb, dtype=np.uint8)
+    if min(a.ndim, b.ndim, sa.ndim, sb.ndim) != 2 or a.shape[0] < M or b.shape[0] < N or \
+            sa.shape[0] < M or sb.shape[0] < N:
+        raise ValueError("operand shapes do not cover M/N")
+    blocks = (K + 31) // 32
+    lda, ldb = max(a.shape[1], K if M == 0 else 0), max(b.shape[1], K if N == 0 else 0)
+    ldsa, ldsb = max(sa.shape[1], blocks if M == 0 else 0), max(sb.shape[1], blocks if N == 0 else 0)
+    if rows is None:
+        rows_arr = None
+        nrows = M
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.size
+    d = np.zeros((nrows, N), dtype=np.float16)
+    bound = np.zeros((nrows, N), dtype=np.float64)
+    total = np.zeros((nrows, N), dtype=np.float64)
+    nt = default_threads() if nthreads is None else nthreads
+    ptr = lambda x: x.ctypes.data if x.size else None
+    rc = _load().oracle_gemm_mxf8(
+        ptr(a), ptr(sa), ptr(b), ptr(sb), ptr(d), ptr(bound), ptr(total),
+        M, N, K, lda, ldsa, ldb, ldsb,
+        rows_arr.ctypes.data if rows_arr is not None and rows_arr.size else None, nrows, nt)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    out_rows = np.arange(M, dtype=np.int64) if rows is None else rows_arr
+    return Result(d, bound, total, out_rows, "f16")
 
 
 def ulp16(x: np.ndarray) -> np.ndarray:

@@ -26,6 +26,10 @@
  * accumulation): the same definition with bfloat16 operands and output.  The
  * pages do not name the output rounding for BF16; the reading taken is the
  * fp16 one, round-to-nearest-even, applied directly from the float64 sum.
+ *
+ * Block-scaled FP8 variant (oracle_gemm_mxf8, at the end of this file): FP8
+ * E4M3 operands with one 8-bit power-of-two scale per 32 K elements of a row,
+ * fp16 output; its definition and readings are written out there.
  */
 #include <math.h>
 #include <pthread.h>
@@ -296,4 +300,151 @@ int oracle_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *D,
 {
     return gemm16(A, B, D, bound, sum, M, N, K, lda, ldb, rows, nrows, nthreads,
                   oracle_bf16_to_double, oracle_double_to_bf16);
+}
+
+/*
+ * Block-scaled FP8 GEMM ("TIRx Layout API", section "Scale Factor 布局":
+ * block-scaled MMA, where the K elements of a row come in groups that share
+ * one 8-bit scale factor; the same page's TMEM section names the
+ * block-scaled FP8 GEMM).  The pages fix neither the element encoding nor the
+ * group length.  The reading taken is OCP MX: elements are FP8 E4M3 (sign,
+ * 4 exponent bits with bias 7, 3 fraction bits; no infinities, S.1111.111 is
+ * NaN, largest finite 448); every 32 consecutive K elements of a row share
+ * one UE8M0 scale byte s worth 2^(s-127) (s = 255 is NaN); the product is
+ * accumulated and rounded to binary16 like the fp16 GEMM:
+ *
+ *   D[i,j] = RNE16( Σ_k (SA[i,k/32]·A[i,k]) · (SB[j,k/32]·B[j,k]) )
+ *
+ * with A[i,k] = A[i*lda+k], SA[i,b] = SA[i*ldsa+b] (bytes), likewise B, SB.
+ * Every term is exact in float64 (two 4-bit significands and powers of two
+ * within float64's range); the sum is taken in increasing k.
+ */
+
+/* E4M3 → float64, exact: exponent 0 is the subnormal range f·2^-9, otherwise
+ * (8+f)·2^(e-10). */
+double oracle_e4m3_to_double(uint8_t b)
+{
+    int sign = (b >> 7) & 1;
+    int e = (b >> 3) & 15;
+    int f = b & 7;
+    double v;
+    if (e == 15 && f == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)f, -9);
+    else
+        v = ldexp((double)(8 | f), e - 10);
+    return sign ? -v : v;
+}
+
+/* UE8M0 scale byte → float64: 2^(s-127), NaN for 255. */
+double oracle_e8m0_to_double(uint8_t s)
+{
+    return s == 255 ? NAN : ldexp(1.0, (int)s - 127);
+}
+
+void oracle_e4m3_to_double_array(const uint8_t *b, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3_to_double(b[i]);
+}
+
+struct mx_job {
+    const uint8_t *A, *SA, *B, *SB;
+    uint16_t *D;
+    double *bound, *sum;
+    int64_t N, K, lda, ldsa, ldb, ldsb;
+    const int64_t *rows;
+    int64_t r_begin, r_end;
+    const double *elut, *slut;
+};
+
+static void *run_rows_mx(void *p)
+{
+    struct mx_job *jb = (struct mx_job *)p;
+    for (int64_t r = jb->r_begin; r < jb->r_end; ++r) {
+        int64_t i = jb->rows ? jb->rows[r] : r;
+        const uint8_t *a = jb->A + i * jb->lda;
+        const uint8_t *sa = jb->SA + i * jb->ldsa;
+        for (int64_t j = 0; j < jb->N; ++j) {
+            const uint8_t *b = jb->B + j * jb->ldb;
+            const uint8_t *sb = jb->SB + j * jb->ldsb;
+            double s = 0.0, bnd = 0.0;
+            for (int64_t k = 0; k < jb->K; ++k) {
+                double x = jb->slut[sa[k / 32]] * jb->elut[a[k]];
+                double y = jb->slut[sb[k / 32]] * jb->elut[b[k]];
+                s += x * y;
+                bnd += fabs(x) * fabs(y);
+            }
+            int64_t o = r * jb->N + j;
+            if (jb->D)
+                jb->D[o] = oracle_double_to_half(s);
+            if (jb->sum)
+                jb->sum[o] = s;
+            if (jb->bound)
+                jb->bound[o] = bnd;
+        }
+    }
+    return NULL;
+}
+
+/* Reference block-scaled GEMM; rows, outputs, threads and the return value as
+ * for oracle_gemm_f16.  ldsa and ldsb count scale bytes per row and must
+ * cover ceil(K/32) blocks. */
+int oracle_gemm_mxf8(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
+                     uint16_t *D, double *bound, double *sum,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb,
+                     const int64_t *rows, int64_t nrows, int nthreads)
+{
+    const int64_t blocks = (K + 31) / 32;
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldsa < blocks || ldsb < blocks || nrows < 0)
+        return -1;
+    if (!rows && nrows != M)
+        return -1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= M)
+                return -1;
+    if (nrows == 0 || N == 0)
+        return 0;
+
+    double elut[256], slut[256];
+    for (int v = 0; v < 256; ++v) {
+        elut[v] = oracle_e4m3_to_double((uint8_t)v);
+        slut[v] = oracle_e8m0_to_double((uint8_t)v);
+    }
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > nrows)
+        nthreads = (int)nrows;
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    struct mx_job *jobs = (struct mx_job *)calloc((size_t)nthreads, sizeof(struct mx_job));
+    if (!th || !jobs) {
+        free(th);
+        free(jobs);
+        return -1;
+    }
+    int64_t per = nrows / nthreads, extra = nrows % nthreads, start = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        int64_t cnt = per + (t < extra ? 1 : 0);
+        struct mx_job jb = {A, SA, B, SB, D, bound, sum, N, K, lda, ldsa, ldb, ldsb, rows,
+                            start, start + cnt, elut, slut};
+        jobs[t] = jb;
+        start += cnt;
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, run_rows_mx, &jobs[t]) != 0)
+            break;
+        started = t;
+    }
+    run_rows_mx(&jobs[0]);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(th[t], NULL);
+    for (int t = started + 1; t < nthreads; ++t)
+        run_rows_mx(&jobs[t]);
+    free(th);
+    free(jobs);
+    return 0;
 }

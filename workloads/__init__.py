@@ -168,3 +168,92 @@ def small_int_pattern(M: int, N: int, K: int, dtype: str = "f16"):
     if dtype == "bf16":
         return to_bf16_bits(a), to_bf16_bits(b)
     return a.astype(np.float16), b.astype(np.float16)
+
+
+# ------------------------------------------------------------ block-scaled FP8
+#
+# Operands of the block-scaled FP8 entry point: FP8 E4M3 codes (uint8) with
+# one UE8M0 scale byte per MX_BLOCK consecutive K elements of every row.
+# Synthetic data are drawn like the fp16 operands (same seeds and
+# distributions) and then encoded the way OCP MX encodes a float block: the
+# block's shared exponent is floor(log2(max |x|)) minus 8 (the largest E4M3
+# exponent; 448 = 1.75·2^8), clamped to [-127, 127] (an all-zero block takes
+# -127), and every element x / 2^exp is rounded to the nearest E4M3 value,
+# ties to the even code, saturating at ±448.  This is input preparation only:
+# the GEMM consumes the codes and scales as given.
+
+MX_BLOCK = 32
+MX_NAN = np.uint8(0x7f)
+
+
+def _e4m3_grid():
+    """The 127 non-negative finite E4M3 values in code order (increasing)."""
+    codes = np.arange(0x7f, dtype=np.int64)
+    e, f = codes >> 3, codes & 7
+    vals = np.where(e == 0, f * 2.0 ** -9, (8 + f) * 2.0 ** (e - 10))
+    return vals, codes.astype(np.uint8)
+
+
+_E4M3_VALS, _E4M3_CODES = _e4m3_grid()
+
+
+def encode_e4m3(q: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code (ties to the even code), saturating at ±448."""
+    q = np.asarray(q, dtype=np.float64)
+    a = np.minimum(np.abs(q), 448.0)
+    i = np.clip(np.searchsorted(_E4M3_VALS, a, side="right") - 1, 0, len(_E4M3_VALS) - 2)
+    lo, hi = _E4M3_VALS[i], _E4M3_VALS[i + 1]
+    up = (hi - a < a - lo) | ((hi - a == a - lo) & ((_E4M3_CODES[i] & 1) == 1))
+    c = np.where(up, _E4M3_CODES[i + 1], _E4M3_CODES[i]).astype(np.uint8)
+    c = np.where(a >= 448.0, np.uint8(0x7e), c)
+    return np.where((q < 0) & (c != 0), c | np.uint8(0x80), c).astype(np.uint8)
+
+
+def mx_quantize(x: np.ndarray):
+    """Encode a float64 (rows, K) matrix as (codes (rows, K) uint8, scales
+    (rows, ceil(K/32)) uint8) with the shared-exponent recipe above."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, K = x.shape
+    nb = (K + MX_BLOCK - 1) // MX_BLOCK
+    padded = np.zeros((rows, nb * MX_BLOCK))
+    padded[:, :K] = x
+    blocks = padded.reshape(rows, nb, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    codes = encode_e4m3(blocks / np.exp2(e)[:, :, None]).reshape(rows, nb * MX_BLOCK)[:, :K]
+    return np.ascontiguousarray(codes), (e + 127).astype(np.uint8)
+
+
+def make_mx_inputs(w: Workload):
+    """Block-scaled FP8 operands for workload ``w``: (A, SA, B, SB), the same
+    float64 draws as ``make_inputs`` encoded with ``mx_quantize``."""
+    a = _draw64(np.random.Generator(np.random.PCG64(SEED_A_BASE + w.index)), (w.M, w.K), w.dist_a)
+    b = _draw64(np.random.Generator(np.random.PCG64(SEED_B_BASE + w.index)), (w.N, w.K), w.dist_b)
+    qa, sa = mx_quantize(a)
+    del a
+    qb, sb = mx_quantize(b)
+    return qa, sa, qb, sb
+
+
+def random_mx(seed: int, rows: int, K: int, scale_lo: int = 120, scale_hi: int = 134):
+    """Seeded random E4M3 codes (every finite code, both signs, NaN codes
+    excluded) with random scale bytes in [scale_lo, scale_hi]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    codes = rng.integers(0, 256, size=(rows, K)).astype(np.uint8)
+    codes = np.where((codes & 0x7f) == 0x7f, codes ^ np.uint8(1), codes).astype(np.uint8)
+    scales = rng.integers(scale_lo, scale_hi + 1, size=(rows, (K + MX_BLOCK - 1) // MX_BLOCK)).astype(np.uint8)
+    return codes, scales
+
+
+def pad_bytes(x: np.ndarray, ld: int, fill: int = 0x7f) -> np.ndarray:
+    """Copy a (rows, n) uint8 matrix into a (rows, ld) buffer padded with
+    ``fill`` (the E4M3 NaN code by default, which is also a NaN-sized scale
+    once it reaches 0xff)."""
+    rows, n = x.shape
+    if ld < n:
+        raise ValueError("leading dimension smaller than the row length")
+    out = np.full((rows, ld), fill, dtype=np.uint8)
+    out[:, :n] = x
+    return out
