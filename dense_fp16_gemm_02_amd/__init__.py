@@ -20,6 +20,7 @@ import ctypes
 import os
 
 __all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_ERR_TOO_LARGE",
+           "TG_ERR_LAYOUT", "tg_gemm_mxf8", "tg_gemm_mxf8_plan",
            "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_gemm_bf16",
            "tg_gemm_bf16_plan", "tg_status_string", "gemm"]
 
@@ -28,6 +29,7 @@ TG_ERR_INVALID_ARG = -1
 TG_ERR_LAUNCH = -2
 TG_ERR_DEVICE = -3
 TG_ERR_TOO_LARGE = -4
+TG_ERR_LAYOUT = -5
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libtg_gemm.so")
@@ -63,6 +65,10 @@ def load():
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64,
                        ctypes.c_char_p, i64, ctypes.POINTER(i64)]
+    lib.tg_gemm_mxf8.restype = ctypes.c_int
+    lib.tg_gemm_mxf8.argtypes = [vp] * 5 + [i64] * 8 + [vp]
+    lib.tg_gemm_mxf8_plan.restype = ctypes.c_int
+    lib.tg_gemm_mxf8_plan.argtypes = [vp] * 5 + [i64] * 8 + [ctypes.c_char_p, i64, ctypes.POINTER(i64)]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -111,6 +117,24 @@ def tg_gemm_bf16_plan(A, B, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: 
     tiles = ctypes.c_int64(0)
     st = load().tg_gemm_bf16_plan(_ptr(A), _ptr(B), _ptr(D), M, N, K, lda, ldb, ldd, buf, 128,
                                   ctypes.byref(tiles))
+    return st, buf.value.decode(), tiles.value
+
+
+def tg_gemm_mxf8(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldsa: int, ldb: int, ldsb: int,
+                 ldd: int, stream=None) -> int:
+    """Enqueue the block-scaled FP8 GEMM (E4M3 bytes A, B; UE8M0 scale bytes
+    SA, SB per 32 K; fp16 D) on ``stream``; returns the C status code."""
+    return load().tg_gemm_mxf8(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldsa, ldb,
+                               ldsb, ldd, _stream(stream))
+
+
+def tg_gemm_mxf8_plan(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldsa: int, ldb: int, ldsb: int,
+                      ldd: int):
+    """Host-only: (status, kernel name, output tile count) for tg_gemm_mxf8."""
+    buf = ctypes.create_string_buffer(128)
+    tiles = ctypes.c_int64(0)
+    st = load().tg_gemm_mxf8_plan(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldsa, ldb,
+                                  ldsb, ldd, buf, 128, ctypes.byref(tiles))
     return st, buf.value.decode(), tiles.value
 
 

@@ -60,6 +60,7 @@ struct Elem<__bf16> {
 };
 
 __host__ __device__ constexpr int imin(int a, int b) { return a < b ? a : b; }
+__host__ __device__ constexpr int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
 constexpr int BK = 64;              // K elements per LDS stage (128 bytes of fp16)
 constexpr int ROW_CHUNKS = BK / 8;  // 16-byte chunks per tile row
@@ -994,6 +995,301 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
     store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
 }
 
+// ------------------------------------------------------------------------
+// Block-scaled FP8 GEMM ("TIRx Layout API", section "Scale Factor 布局": a
+// block-scaled MMA reads, besides its operands, one 8-bit scale factor per
+// group of K elements of every row, and the scale factors are laid out so
+// that each lane window that consumes a row sees its row's factors).  Read as
+// OCP MX: E4M3 operand bytes, one UE8M0 scale byte per 32 K elements of a
+// row, fp32 accumulation, fp16 output rounded to nearest even.
+//
+// gfx950 does the scaling inside the matrix core: v_mfma_scale_f32_32x32x64
+// takes per lane a 32-byte operand slice and a 32-bit scale register whose
+// low byte scales one 32-element block.  Its lane map (probed on the device):
+// lane l = r + 32·h holds row r; its bytes 0..15 are K 16h..16h+15 and bytes
+// 16..31 are K 32+16h..32+16h+15 of the instruction's 64 K, so it reads
+// 16-byte chunks h and 2+h of the K-step; and the scale byte of lane r + 32·h
+// applies to block h (K 32h..32h+31) of row r, on either operand.  With the
+// MFMA inputs swapped as in the fp16 kernels (B feeds the first input), the
+// accumulator map is the 32×32 one of v_mfma_f32_32x32x16_f16.
+//
+// Everything else follows gemm_dma3_kernel: a 256×256 tile, four waves of
+// 128×128, 128-byte operand rows in LDS (128 K per stage, two 64-K MFMA
+// K-steps per stage) with the same swizzle and source-side DMA addressing,
+// three A stages and two B stages.  Per iteration t:
+//   K-step 0: the scale words of K-tile t+1 are loaded (eight 4-byte loads
+//             per lane, one per fragment row), then A(t+2) is DMAed;
+//   wait until all but A(t+2) has landed; barrier;
+//   K-step 1: B(t+2) is DMAed while the fragments of K-tile t+1's K-step 0
+//             are read.
+// A scale word holds the four blocks of one row in one K-tile; lane r + 32·h
+// feeds the MFMA of K-step kk the byte for block 2·kk + h, and blocks at or
+// past K/32 (the tail of the last K-tile, whose operand bytes are zero) read
+// as 2^0 instead of whatever the padding holds.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__host__ __device__ constexpr int mx_row_of(int l) { return l & 31; }
+__host__ __device__ constexpr int mx_chunk_of(int l, int kk, int half) { return 4 * kk + 2 * half + (l >> 5); }
+constexpr bool mx_fragment_covers_k_step()
+{
+    // every (row, K) of a 32-row, 64-K step is read by exactly one lane byte
+    bool seen[32 * 64] = {};
+    for (int l = 0; l < 64; ++l)
+        for (int half = 0; half < 2; ++half)
+            for (int e = 0; e < 16; ++e) {
+                const int k = 16 * mx_chunk_of(l, 0, half) + e;
+                const int idx = mx_row_of(l) * 64 + k;
+                if (k >= 64 || seen[idx])
+                    return false;
+                seen[idx] = true;
+            }
+    return true;
+}
+static_assert(mx_fragment_covers_k_step(), "scaled-MFMA fragment reads must cover the K-step once");
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ SB, _Float16 *__restrict__ D, int M, int N, int K, int64_t lda,
+    int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd, int tiles_m, int tiles_n, int dvec)
+{
+    using E = _Float16;
+    using V4 = Elem<E>::v4;
+    constexpr int BKB = 128;  // K elements (= bytes) per stage row
+    constexpr int SA_ = 3, SB_ = 2;
+    using T = OperandTile<64>;  // 128-byte rows; T::off counts 2-byte units
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int KSTEPS = BKB / 64;
+    constexpr int A_PASSES = BM / T::ROWS_PER_DMA / NW, B_PASSES = BN / T::ROWS_PER_DMA / NW;
+    constexpr int STAGE_A = BM * BKB, STAGE_B = BN * BKB;  // bytes
+    constexpr int NFRAG = TM + TN;
+    constexpr int SLOTS = TM * TN;
+    static_assert(KSTEPS == 2 && SLOTS == 2 * NFRAG, "two K-steps; one fragment half read per slot");
+    static_assert((BM / T::ROWS_PER_DMA) % NW == 0 && (BN / T::ROWS_PER_DMA) % NW == 0,
+                  "DMA row groups must split evenly over the waves");
+    static_assert(SA_ * STAGE_A + SB_ * STAGE_B <= 160 * 1024, "LDS budget");
+    static_assert(2 * NFRAG + A_PASSES + B_PASSES + A_PASSES <= 63, "vmcnt holds 6 bits");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SA_ * STAGE_A + SB_ * STAGE_B];
+    uint8_t *const a_ring = smem;
+    uint8_t *const b_ring = smem + SA_ * STAGE_A;
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    const int dr = lane / T::RC, dpc = lane % T::RC;
+    uint32_t a_off[A_PASSES], b_off[B_PASSES];
+    int a_kc[A_PASSES], b_kc[B_PASSES];
+#pragma unroll
+    for (int p = 0; p < A_PASSES; ++p) {
+        const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
+        a_kc[p] = dpc ^ T::swz(t);
+        a_off[p] = (uint32_t)(imin(t, M - 1 - m0) * lda + 16 * a_kc[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < B_PASSES; ++p) {
+        const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
+        b_kc[p] = dpc ^ T::swz(t);
+        b_off[p] = (uint32_t)(imin(t, N - 1 - n0) * ldb + 16 * b_kc[p]);
+    }
+    const uint8_t *a_tile = A + (int64_t)m0 * lda;
+    const uint8_t *b_tile = B + (int64_t)n0 * ldb;
+    const int KT = (K + BKB - 1) / BKB;
+    const int nblk = K / 32;
+
+    struct Op {
+        __amdgpu_buffer_rsrc_t r;
+        uint8_t *dst;
+        int klim;
+    };
+    auto op_a = [&](int t) {
+        Op o;
+        o.r = __builtin_amdgcn_make_buffer_rsrc((void *)(a_tile + t * BKB), (short)0, DMA_RANGE,
+                                                BUFFER_RSRC_WORD3);
+        o.dst = a_ring + (t % SA_) * STAGE_A;
+        o.klim = t < KT ? K - t * BKB : 0;
+        return o;
+    };
+    auto op_b = [&](int t) {
+        Op o;
+        o.r = __builtin_amdgcn_make_buffer_rsrc((void *)(b_tile + t * BKB), (short)0, DMA_RANGE,
+                                                BUFFER_RSRC_WORD3);
+        o.dst = b_ring + (t % SB_) * STAGE_B;
+        o.klim = t < KT ? K - t * BKB : 0;
+        return o;
+    };
+    auto dma_a = [&](const Op &o, int p) {
+        dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BKB,
+                           16 * a_kc[p] < o.klim ? a_off[p] : DMA_OOB);
+    };
+    auto dma_b = [&](const Op &o, int p) {
+        dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BKB,
+                           16 * b_kc[p] < o.klim ? b_off[p] : DMA_OOB);
+    };
+
+    // Scale words: a buffer over the rows from m0 (n0) on, so rows past M
+    // (N), which feed only unstored outputs, read as zero words.
+    const int srow = mx_row_of(lane), shalf = lane >> 5;
+    const __amdgpu_buffer_rsrc_t sa_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(SA + (int64_t)m0 * ldsa), (short)0, (int)imin64((int64_t)(M - m0) * ldsa, DMA_RANGE),
+        BUFFER_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t sb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(SB + (int64_t)n0 * ldsb), (short)0, (int)imin64((int64_t)(N - n0) * ldsb, DMA_RANGE),
+        BUFFER_RSRC_WORD3);
+    const uint32_t sa_off = (uint32_t)((wm * WTM + srow) * ldsa), sb_off = (uint32_t)((wn * WTN + srow) * ldsb);
+    const uint32_t sa_step = (uint32_t)(32 * ldsa), sb_step = (uint32_t)(32 * ldsb);
+    uint32_t sw_a[2][TM], sw_b[2][TN];  // scale words: [current, next K-tile]
+    auto load_scales = [&](int t, uint32_t *wa, uint32_t *wb) {
+#pragma unroll
+        for (int q = 0; q < TM; ++q)
+            wa[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(sa_rsrc, (int)(sa_off + q * sa_step + 4 * t), 0, 0);
+#pragma unroll
+        for (int q = 0; q < TN; ++q)
+            wb[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(sb_rsrc, (int)(sb_off + q * sb_step + 4 * t), 0, 0);
+    };
+    // scale register for K-step kk of K-tile t from its word: block 4t+2kk+h
+    auto scale_of = [&](uint32_t w, int t, int kk) {
+        const int blk = 4 * t + 2 * kk + shalf;
+        return blk < nblk ? (int)(w >> (16 * kk + 8 * shalf)) : 127;
+    };
+
+    i32x8 fa[2][TM], fb[2][TN];
+    auto read_frag = [&](int sa, int sb, int kk, int q, int half, i32x8 *a, i32x8 *b) {
+        const int c = mx_chunk_of(lane, kk, half);
+        const uint8_t *src = q < TM ? a_ring + sa * STAGE_A + 2 * T::off(wm * WTM + q * 32 + srow, c)
+                                    : b_ring + sb * STAGE_B + 2 * T::off(wn * WTN + (q - TM) * 32 + srow, c);
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(src);
+        i32x8 &f = q < TM ? a[q] : b[q - TM];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            f[4 * half + e] = v[e];
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[i][j][v] = 0.0f;
+
+    auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
+    // One K-step of K-tile t: MFMA per slot; after MFMA i, half i%2 of the
+    // next step's fragment i/2; DMA passes [0, n) of `o` in the odd slots.
+    auto step = [&](const i32x8 *a, const i32x8 *b, const uint32_t *wa, const uint32_t *wb, int t, int kk,
+                    bool with_reads, int rsa, int rsb, int rkk, i32x8 *na, i32x8 *nb, const Op *o, bool is_a,
+                    int n) {
+        int sa_reg[TM], sb_reg[TN];
+#pragma unroll
+        for (int q = 0; q < TM; ++q)
+            sa_reg[q] = scale_of(wa[q], t, kk);
+#pragma unroll
+        for (int q = 0; q < TN; ++q)
+            sb_reg[q] = scale_of(wb[q], t, kk);
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int ti = i / TN, tj = i % TN;
+            acc[ti][tj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[tj], a[ti], acc[ti][tj], 0, 0, 0,
+                                                                          sb_reg[tj], 0, sa_reg[ti]);
+            MFMA_FIRST();
+            if (with_reads)
+                read_frag(rsa, rsb, rkk, frag_of_slot(i / 2), i % 2, na, nb);
+            if (o && (i % 2) == 1 && i / 2 < n) {
+                if (is_a)
+                    dma_a(*o, i / 2);
+                else
+                    dma_b(*o, i / 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // prologue: scale words of K-tile 0, then A(0), B(0), A(1), B(1)
+    if (KT > 0)
+        load_scales(0, sw_a[0], sw_b[0]);
+    {
+        const Op a0 = op_a(0), b0 = op_b(0), a1 = op_a(1), b1 = op_b(1);
+#pragma unroll
+        for (int p = 0; p < A_PASSES; ++p)
+            dma_a(a0, p);
+#pragma unroll
+        for (int p = 0; p < B_PASSES; ++p)
+            dma_b(b0, p);
+#pragma unroll
+        for (int p = 0; p < A_PASSES; ++p)
+            dma_a(a1, p);
+#pragma unroll
+        for (int p = 0; p < B_PASSES; ++p)
+            dma_b(b1, p);
+    }
+    wait_vmem<A_PASSES + B_PASSES>();
+    barrier_lds();
+#pragma unroll
+    for (int q = 0; q < NFRAG; ++q) {
+        read_frag(0, 0, 0, q, 0, fa[0], fb[0]);
+        read_frag(0, 0, 0, q, 1, fa[0], fb[0]);
+    }
+
+    int sa = 0, sb = 0;
+    for (int kt = 0; kt < KT - 1; ++kt) {
+        load_scales(kt + 1, sw_a[1], sw_b[1]);
+        const Op an = op_a(kt + 2);
+        step(fa[0], fb[0], sw_a[0], sw_b[0], kt, 0, true, sa, sb, 1, fa[1], fb[1], &an, true, A_PASSES);
+        wait_vmem<A_PASSES>();  // B(kt+1), A(kt+1) and the scale words of kt+1 have landed
+        barrier_lds();
+        const Op b2 = op_b(kt + 2);
+        const int sa1 = sa + 1 == SA_ ? 0 : sa + 1, sb1 = sb + 1 == SB_ ? 0 : sb + 1;
+        step(fa[1], fb[1], sw_a[0], sw_b[0], kt, 1, true, sa1, sb1, 0, fa[0], fb[0], &b2, false, B_PASSES);
+        sa = sa1;
+        sb = sb1;
+#pragma unroll
+        for (int q = 0; q < TM; ++q)
+            sw_a[0][q] = sw_a[1][q];
+#pragma unroll
+        for (int q = 0; q < TN; ++q)
+            sw_b[0][q] = sw_b[1][q];
+    }
+    if (KT > 0) {
+        step(fa[0], fb[0], sw_a[0], sw_b[0], KT - 1, 0, true, sa, sb, 1, fa[1], fb[1], nullptr, false, 0);
+        step(fa[1], fb[1], sw_a[0], sw_b[0], KT - 1, 1, false, 0, 0, 0, fa[0], fb[0], nullptr, false, 0);
+    }
+    wait_vmem<0>();
+
+    // staged epilogue, as in gemm_dma3_kernel
+    static_assert(NW * WTM * WTN * 2 <= SA_ * STAGE_A + SB_ * STAGE_B, "staging fits in the stage memory");
+    constexpr int SROW = WTN;
+    constexpr int SCH = WTN / 8;
+    static_assert((SCH & (SCH - 1)) == 0 && SCH >= 2, "chunk swizzle needs a power of two");
+    auto stage_off = [](int r, int chunk) { return r * SROW + ((chunk ^ (r & (SCH - 1))) << 3); };
+    barrier_lds();
+    E *stg = reinterpret_cast<E *>(smem) + wave * WTM * WTN;
+    const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                V4 h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    h[r] = (E)acc[i][j][g * 4 + r];  // round to nearest even
+                const int r = i * 32 + frag_row;
+                const int c = j * 32 + g * 8 + frag_hi * 4;
+                *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
+            }
+    store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
+}
+
 struct KernelChoice {
     const void *fn;
     const char *tile;  // "<BM>x<BN>_w<WM>x<WN>"
@@ -1259,6 +1555,72 @@ extern "C" int tg_gemm_bf16_plan(const void *A, const void *B, const void *D, in
     return plan<__bf16>(A, B, D, M, N, K, lda, ldb, ldd, name, name_len, tiles);
 }
 
+// Block-scaled FP8 entry point: argument checks, then one 256×256 tile per
+// workgroup.
+constexpr const char *MXF8_KERNEL = "gemm_mxf8_256x256_w2x2_dma";
+
+int validate_mx(const void *A, const void *SA, const void *B, const void *SB, const void *D, int64_t M,
+                int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd)
+{
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldd < N || ldsa < (K + 31) / 32 ||
+        ldsb < (K + 31) / 32 || lda < 0 || ldb < 0 || ldsa < 0 || ldsb < 0 || ldd < 0)
+        return TG_ERR_INVALID_ARG;
+    if ((M > 0 && K > 0 && (!A || !SA)) || (N > 0 && K > 0 && (!B || !SB)) || (M > 0 && N > 0 && !D))
+        return TG_ERR_INVALID_ARG;
+    if (M >= LIMIT32 || N >= LIMIT32 || K >= LIMIT32 || lda >= LIMIT32 || ldb >= LIMIT32 ||
+        ldd >= LIMIT32 || 255 * lda + 128 >= DMA_RANGE || 255 * ldb + 128 >= DMA_RANGE ||
+        256 * ldsa + 4 * K >= LIMIT32 || 256 * ldsb + 4 * K >= LIMIT32)
+        return TG_ERR_TOO_LARGE;
+    if (K % 32 != 0 || lda % 16 != 0 || ldb % 16 != 0 || ldsa % 4 != 0 || ldsb % 4 != 0 ||
+        (uintptr_t)A % 16 != 0 || (uintptr_t)B % 16 != 0 || (uintptr_t)SA % 4 != 0 || (uintptr_t)SB % 4 != 0)
+        return TG_ERR_LAYOUT;
+    return TG_OK;
+}
+
+extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const void *SB, void *D,
+                            int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb,
+                            int64_t ldsb, int64_t ldd, void *stream)
+{
+    int st = validate_mx(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd);
+    if (st != TG_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    st = check_device();
+    if (st != TG_OK)
+        return st;
+    int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
+    const int64_t grid = (int64_t)tiles_m * tiles_n;
+    if (grid >= LIMIT32)
+        return TG_ERR_TOO_LARGE;
+    int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+    int dvec = (ldd % 8 == 0) && ((uintptr_t)D % 16 == 0);
+    void *args[] = {(void *)&A, (void *)&SA, (void *)&B, (void *)&SB, (void *)&D, &Mi, &Ni, &Ki,
+                    &lda, &ldsa, &ldb, &ldsb, &ldd, &tiles_m, &tiles_n, &dvec};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2>),
+                                   dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+extern "C" int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, const void *SB,
+                                 const void *D, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                 int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd, char *name,
+                                 int64_t name_len, int64_t *tiles)
+{
+    int st = validate_mx(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd);
+    if (name && name_len > 0)
+        name[0] = 0;
+    if (tiles)
+        *tiles = 0;
+    if (st != TG_OK || M == 0 || N == 0)
+        return st;
+    if (name && name_len > 0)
+        snprintf(name, (size_t)name_len, "%s", MXF8_KERNEL);
+    if (tiles)
+        *tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    return TG_OK;
+}
+
 extern "C" const char *tg_status_string(int status)
 {
     switch (status) {
@@ -1272,6 +1634,8 @@ extern "C" const char *tg_status_string(int status)
         return "no usable gfx950 device";
     case TG_ERR_TOO_LARGE:
         return "dimension exceeds the 32-bit range the kernels address";
+    case TG_ERR_LAYOUT:
+        return "block-scaled layout not supported (K % 32, lda/ldb % 16, ldsa/ldsb % 4, or alignment)";
     default:
         return "unknown status";
     }

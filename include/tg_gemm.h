@@ -39,7 +39,11 @@ enum {
     /* a dimension or index exceeds what the kernels address (each of M, N,
      * K, lda, ldb, ldd must be below 2^31, and A, B, D must each span fewer
      * than 2^62 elements).  Nothing is launched. */
-    TG_ERR_TOO_LARGE = -4
+    TG_ERR_TOO_LARGE = -4,
+    /* tg_gemm_mxf8 only: K is not a multiple of 32, lda or ldb not a
+     * multiple of 16, ldsa or ldsb not a multiple of 4, A or B not 16-byte
+     * aligned, or SA or SB not 4-byte aligned.  Nothing is launched. */
+    TG_ERR_LAYOUT = -5
 };
 
 /*
@@ -107,6 +111,53 @@ int tg_gemm_bf16(const void *A, const void *B, void *D,
 int tg_gemm_bf16_plan(const void *A, const void *B, const void *D,
                       int64_t M, int64_t N, int64_t K,
                       int64_t lda, int64_t ldb, int64_t ldd,
+                      char *name, int64_t name_len, int64_t *tiles);
+
+/*
+ * tg_gemm_mxf8 — block-scaled FP8 GEMM:
+ *
+ *   D[i,j] ← fp16_rne( Σ_k (2^(SA[i,k/32]-127)·A[i,k]) · (2^(SB[j,k/32]-127)·B[j,k]) )
+ *
+ * "TIRx Layout API", section "Scale Factor 布局": a block-scaled MMA reads
+ * one 8-bit scale factor per group of K elements of every row besides its
+ * operands (the page's example is a block-scaled FP8 GEMM).  The pages fix
+ * neither the encodings nor the group length; this entry point takes the
+ * OCP MX reading: A and B hold FP8 E4M3 codes (bias 7, no infinities,
+ * S.1111.111 is NaN, largest finite 448), and every 32 consecutive K elements
+ * of a row share one UE8M0 scale byte worth 2^(s-127) (255 is NaN).  Products
+ * are accumulated in fp32 and D is binary16, rounded to nearest even.
+ *
+ *   A    device pointer, M×K bytes, row i at A + i·lda; 16-byte aligned.
+ *   SA   device pointer, M×ldsa scale bytes, SA[i,b] = SA[i·ldsa + b] for
+ *        blocks b < K/32; 4-byte aligned.  Bytes past K/32 in a row are
+ *        never used (they may hold anything).
+ *   B    device pointer, N×K bytes (the weight, stored like A), row j at
+ *        B + j·ldb; 16-byte aligned.
+ *   SB   device pointer, N×ldsb scale bytes, like SA.
+ *   D    device pointer to binary16, M×N window with leading dimension ldd
+ *        (elements); written only inside the window.
+ *   K    a multiple of 32 (whole scale blocks); K == 0 sets D's window to +0.
+ *   lda, ldb   bytes between rows, >= K and multiples of 16.
+ *   ldsa, ldsb bytes between scale rows, >= K/32 and multiples of 4.
+ *   stream     as for tg_gemm_f16.
+ *
+ * Ownership, threading, asynchrony and edge cases in M and N are as for
+ * tg_gemm_f16.  Returns TG_OK, TG_ERR_INVALID_ARG (negative sizes, a
+ * leading dimension too small, a NULL pointer with elements behind it),
+ * TG_ERR_LAYOUT (the multiple-of and alignment rules above),
+ * TG_ERR_TOO_LARGE, TG_ERR_DEVICE or TG_ERR_LAUNCH.
+ */
+int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const void *SB, void *D,
+                 int64_t M, int64_t N, int64_t K,
+                 int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd,
+                 void *stream);
+
+/* tg_gemm_mxf8_plan — host-only: the kernel name ("gemm_mxf8_…") and tile
+ * count tg_gemm_mxf8 would use, and its argument-validation status; outputs
+ * as for tg_gemm_f16_plan. */
+int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, const void *SB, const void *D,
+                      int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd,
                       char *name, int64_t name_len, int64_t *tiles);
 
 /* tg_status_string — a static, NUL-terminated description of a status. */

@@ -130,3 +130,43 @@ def test_bf16_plans_and_validation():
     assert tg.tg_gemm_bf16(FAKE, FAKE, FAKE, 4, 4, 8, 4, 8, 4, None) == tg.TG_ERR_INVALID_ARG
     assert tg.tg_gemm_bf16(FAKE, FAKE, FAKE, 1 << 31, 4, 4, 4, 4, 4, None) == tg.TG_ERR_TOO_LARGE
     assert tg.tg_gemm_bf16(None, None, None, 0, 0, 0, 0, 0, 0, None) == tg.TG_OK
+
+
+def test_mxf8_plans_and_validation():
+    """Host-side checks of the block-scaled entry point: plans for the
+    workloads whose K is whole 32-element blocks, and every rejection rule
+    (none of these calls reaches a device)."""
+    for w in workloads.WORKLOADS:
+        nb = (w.K // 32 + 3) // 4 * 4
+        st, name, tiles = tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, w.M, w.N, w.K, w.K, nb, w.K, nb, w.N)
+        if w.K % 32:
+            assert st == tg.TG_ERR_LAYOUT and name == "" and tiles == 0
+            continue
+        assert st == tg.TG_OK and name == "gemm_mxf8_256x256_w2x2_dma"
+        assert tiles == ((w.M + 255) // 256) * ((w.N + 255) // 256)
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 128, 128, 4, 128, 4, 64)
+    assert tg.tg_gemm_mxf8_plan(*ok)[0] == tg.TG_OK
+
+    def with_(**kw):
+        names = ["A", "SA", "B", "SB", "D", "M", "N", "K", "lda", "ldsa", "ldb", "ldsb", "ldd"]
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return tg.tg_gemm_mxf8_plan(*args)[0], tg.tg_gemm_mxf8(*args, None)
+
+    for kw, want in [({"K": 100, "lda": 128, "ldb": 128}, tg.TG_ERR_LAYOUT),
+                     ({"lda": 136}, tg.TG_ERR_LAYOUT), ({"ldb": 200}, tg.TG_ERR_LAYOUT),
+                     ({"ldsa": 6}, tg.TG_ERR_LAYOUT), ({"ldsb": 5}, tg.TG_ERR_LAYOUT),
+                     ({"A": FAKE + 8}, tg.TG_ERR_LAYOUT), ({"B": FAKE + 4}, tg.TG_ERR_LAYOUT),
+                     ({"SA": FAKE + 2}, tg.TG_ERR_LAYOUT), ({"SB": FAKE + 1}, tg.TG_ERR_LAYOUT),
+                     ({"lda": 112}, tg.TG_ERR_INVALID_ARG), ({"ldsa": 3}, tg.TG_ERR_INVALID_ARG),
+                     ({"ldd": 63}, tg.TG_ERR_INVALID_ARG), ({"M": -1}, tg.TG_ERR_INVALID_ARG),
+                     ({"SA": None}, tg.TG_ERR_INVALID_ARG), ({"SB": None}, tg.TG_ERR_INVALID_ARG),
+                     ({"D": None}, tg.TG_ERR_INVALID_ARG),
+                     ({"M": 1 << 31}, tg.TG_ERR_TOO_LARGE), ({"lda": 1 << 24}, tg.TG_ERR_TOO_LARGE),
+                     ({"ldsb": 1 << 23}, tg.TG_ERR_TOO_LARGE)]:
+        assert with_(**kw) == (want, want), kw
+    # empty problems launch nothing and need no pointers
+    assert tg.tg_gemm_mxf8(None, None, None, None, None, 0, 0, 0, 0, 0, 0, 0, 0, None) == tg.TG_OK
+    assert tg.tg_gemm_mxf8_plan(None, None, FAKE, FAKE, None, 0, 7, 64, 64, 4, 64, 4, 7) == (tg.TG_OK, "", 0)
+    assert tg.tg_status_string(tg.TG_ERR_LAYOUT) != "unknown status"

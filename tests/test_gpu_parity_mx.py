@@ -1,0 +1,209 @@
+"""GPU parity of tg_gemm_mxf8 (through the C ABI) against the CPU oracle's
+block-scaled FP8 GEMM on the same seeded inputs.
+
+Acceptance per checked element: |D − ref| ≤ 4e-3·Σ_k|sa·a||sb·b| + ulp16(ref),
+D finite; where every partial sum is exact in fp32 the comparison is
+bit-exact.  Covered: the workloads whose K is whole 32-element blocks (small
+ones on every element, the large ones on sampled rows; the ragged 1000³ case
+runs at K = 992), exact operands that make every block's scale visible, a
+partial last K-tile, tails in M and N with a guard band around D, padding of
+operands and scale rows holding NaN codes, K = 0, and the layout errors."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import SENTINEL, say
+
+torch = pytest.importorskip("torch")
+tg = pytest.importorskip("dense_fp16_gemm_02_amd")
+
+pytestmark = pytest.mark.gpu
+
+ONE, MINUS_ONE, ZERO = 0x38, 0xb8, 0x00
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tg.load()
+    torch.cuda.init()
+
+
+def _bytes(x: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to("cuda:0")
+
+
+def run_mx(a, sa, b, sb, M, N, K, guard=0, label=""):
+    """D (M, N) fp16 window and the full (M+2g, N+2g) buffer (uint16) of
+    tg_gemm_mxf8 on byte arrays a (M, lda), sa (M, ldsa), b (N, ldb), sb
+    (N, ldsb); every byte in them is passed to the device as is."""
+    lda, ldsa, ldb, ldsb = a.shape[1], sa.shape[1], b.shape[1], sb.shape[1]
+    ldd = N + 2 * guard
+    A, SA, B, SB = _bytes(a), _bytes(sa), _bytes(b), _bytes(sb)
+    d = torch.full(((M + 2 * guard) * ldd + 8,), SENTINEL, dtype=torch.int16, device="cuda:0")
+    dptr = d.data_ptr() + 2 * (guard * ldd + guard)
+    say(f"mxf8 {label} M={M} N={N} K={K} lda={lda} ldsa={ldsa} ldb={ldb} ldsb={ldsb} guard={guard}")
+    st = tg.tg_gemm_mxf8(A, SA, B, SB, dptr, M, N, K, lda, ldsa, ldb, ldsb, ldd, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    full = d.cpu().numpy().view(np.uint16)[:(M + 2 * guard) * ldd].reshape(M + 2 * guard, ldd)
+    win = np.array(full[guard:guard + M, guard:guard + N].view(np.float16))
+    return win, full, st
+
+
+def _guard_ok(full, M, N, g):
+    mask = np.ones(full.shape, bool)
+    mask[g:g + M, g:g + N] = False
+    return bool(np.all(full[mask] == SENTINEL))
+
+
+def _check(d, res, what):
+    ok, worst, report = oracle.check(d, res)
+    assert ok, f"{what}: {report}"
+
+
+def _padded_scales(s, ld, fill=0xff):
+    """Scale rows padded to ld bytes with NaN scale bytes (never to be used)."""
+    return workloads.pad_bytes(s, ld, fill)
+
+
+def _ld4(n):
+    return max(4, (n + 3) // 4 * 4)
+
+
+SMALL = [w for w in workloads.WORKLOADS if w.M * w.N * w.K <= 2 ** 31]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_workloads_every_element(w):
+    K = w.K - w.K % 32  # the ragged 1000³ case runs at K = 992
+    qa, sa, qb, sb = workloads.make_mx_inputs(dataclasses.replace(w, K=K))
+    res = oracle.gemm_mx(qa, sa, qb, sb, w.M, w.N, K)
+    d, full, st = run_mx(qa, _padded_scales(sa, _ld4(K // 32)), qb, _padded_scales(sb, _ld4(K // 32)),
+                         w.M, w.N, K, guard=3, label=w.name)
+    assert st == tg.TG_OK
+    _check(d, res, w.name)
+    assert _guard_ok(full, w.M, w.N, 3)
+
+
+@pytest.mark.parametrize("w", [w for w in workloads.WORKLOADS if w.M * w.N * w.K > 2 ** 31], ids=lambda w: w.name)
+def test_large_workloads_sampled_rows(w):
+    qa, sa, qb, sb = workloads.make_mx_inputs(w)
+    rows = workloads.sample_rows(w)
+    res = oracle.gemm_mx(qa, sa, qb, sb, w.M, w.N, w.K, rows=rows)
+    d, _, st = run_mx(qa, sa, qb, sb, w.M, w.N, w.K, label=w.name)
+    assert st == tg.TG_OK
+    _check(d[rows], res, w.name)
+    assert np.all(np.isfinite(d.astype(np.float32)))
+
+
+def _pm1(seed, rows, K):
+    rng = np.random.default_rng(seed)
+    return rng.choice(np.array([ONE, MINUS_ONE, ZERO], np.uint8), size=(rows, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 520, 256), (77, 600, 1024), (513, 129, 96)])
+def test_unit_scales_exact(M, N, K):
+    """Values in {-1, 0, 1} with unit scales: D is an integer ≤ K, exact in
+    fp32 and fp16, so every element must match the oracle bit for bit."""
+    a, b = _pm1(11 + K, M, K), _pm1(12 + K, N, K)
+    sa = np.full((M, _ld4(K // 32)), 127, np.uint8)
+    sb = np.full((N, _ld4(K // 32)), 127, np.uint8)
+    res = oracle.gemm_mx(a, sa, b, sb, M, N, K)
+    d, full, st = run_mx(a, sa, b, sb, M, N, K, guard=2, label="unit scales")
+    assert st == tg.TG_OK
+    assert np.array_equal(d.view(np.uint16), res.d.view(np.uint16))
+    assert _guard_ok(full, M, N, 2)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (190, 333, 384), (260, 260, 96)])
+def test_random_scales_exact(M, N, K):
+    """Values ±1 and 0 with scales 2^-3..2^3 per block: every partial sum is a
+    multiple of 2^-6 below 2^12, exact in fp32, so D is bit-exact.  A scale
+    applied to the wrong block, lane half or operand changes D."""
+    a, b = _pm1(21 + K, M, K), _pm1(22 + K, N, K)
+    rng = np.random.default_rng(23 + K)
+    nb = K // 32
+    sa = _padded_scales(rng.integers(124, 131, size=(M, nb)).astype(np.uint8), _ld4(nb))
+    sb = _padded_scales(rng.integers(124, 131, size=(N, nb)).astype(np.uint8), _ld4(nb))
+    res = oracle.gemm_mx(a, sa, b, sb, M, N, K)
+    d, _, st = run_mx(a, sa, b, sb, M, N, K, label="random scales")
+    assert st == tg.TG_OK
+    assert np.array_equal(d.view(np.uint16), res.d.view(np.uint16))
+
+
+@pytest.mark.parametrize("side", ["a", "b"])
+def test_each_block_scale_lands_on_its_block(side):
+    """All-ones operands with unit scales except one block of one row per
+    probe: that row (column) of D gains exactly 7·32, nothing else moves."""
+    M, N, K = 260, 270, 224   # two K-tiles, the second partial (blocks 4..6)
+    nb = K // 32
+    ones_a = np.full((M, K), ONE, np.uint8)
+    ones_b = np.full((N, K), ONE, np.uint8)
+    for probe, (row, blk) in enumerate([(0, 0), (1, 1), (33, 2), (31, 3), (64, 4), (259 if side == "a" else 269, 6)]):
+        sa = _padded_scales(np.full((M, nb), 127, np.uint8), 8)
+        sb = _padded_scales(np.full((N, nb), 127, np.uint8), 8)
+        (sa if side == "a" else sb)[row, blk] = 130
+        d, _, st = run_mx(ones_a, sa, ones_b, sb, M, N, K, label=f"block probe {side} {row},{blk}")
+        assert st == tg.TG_OK
+        want = np.full((M, N), float(K))
+        if side == "a":
+            want[row, :] += 7 * 32
+        else:
+            want[:, row] += 7 * 32
+        assert np.array_equal(d.astype(np.float64), want), f"probe {probe}: row {row} block {blk}"
+
+
+@pytest.mark.parametrize("K", [32, 96, 160, 4096 + 96])
+def test_partial_k_tiles_and_nan_padding(K):
+    """K not a multiple of the 128-element stage: the missing elements are
+    read as zero and their scale bytes (NaN here) are never applied; operand
+    padding past K holds the NaN code."""
+    M, N = 300, 280
+    # scales 2^-15..2^-9 keep |D| far below fp16's range for any codes
+    qa, sa = workloads.random_mx(31 + K, M, K, 112, 118)
+    qb, sb = workloads.random_mx(32 + K, N, K, 112, 118)
+    nb = K // 32
+    a = workloads.pad_bytes(qa, K + 48)
+    b = workloads.pad_bytes(qb, K + 16 * 5)
+    sa_p = _padded_scales(sa, _ld4(nb) + 4)
+    sb_p = _padded_scales(sb, _ld4(nb))
+    res = oracle.gemm_mx(qa, sa, qb, sb, M, N, K)
+    d, full, st = run_mx(a, sa_p, b, sb_p, M, N, K, guard=2, label="partial K")
+    assert st == tg.TG_OK
+    _check(d, res, f"K={K}")
+    assert _guard_ok(full, M, N, 2)
+
+
+def test_zero_k_and_empty():
+    a = np.zeros((5, 16), np.uint8)
+    s = np.zeros((5, 4), np.uint8)
+    d, full, st = run_mx(a, s, a, s, 5, 5, 0, guard=1, label="K=0")
+    assert st == tg.TG_OK and np.all(d == 0) and not np.signbit(d).any()
+    assert _guard_ok(full, 5, 5, 1)
+    assert tg.tg_gemm_mxf8(0, 0, 0, 0, 0, 0, 5, 0, 32, 4, 32, 4, 5, None) == tg.TG_OK
+
+
+def test_layout_errors():
+    a = torch.zeros(64 * 160, dtype=torch.uint8, device="cuda:0")
+    s = torch.zeros(64 * 8, dtype=torch.uint8, device="cuda:0")
+    d = torch.zeros(64 * 64, dtype=torch.float16, device="cuda:0")
+    p, q, r = a.data_ptr(), s.data_ptr(), d.data_ptr()
+    ok = (p, q, p, q, r, 64, 64, 128, 160, 4, 160, 4, 64, None)
+    assert tg.tg_gemm_mxf8(*ok) == tg.TG_OK
+    for bad in [dict(K=100, lda=160, ldb=160), dict(K=128, lda=136), dict(K=128, ldsa=5, ldsa_ok=False),
+                dict(K=128, a_off=8), dict(K=128, s_off=2)]:
+        args = list(ok)
+        args[7] = bad.get("K", 128)
+        args[8] = bad.get("lda", 160)
+        args[9] = bad.get("ldsa", 4)
+        args[0] = p + bad.get("a_off", 0)
+        args[1] = q + bad.get("s_off", 0)
+        say(f"mxf8 layout error {bad}")
+        assert tg.tg_gemm_mxf8(*args) == tg.TG_ERR_LAYOUT, bad
+    assert tg.tg_gemm_mxf8(p, q, p, q, r, 64, 64, 128, 100, 4, 160, 4, 64, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_mxf8(p, q, p, q, r, 64, 64, 128, 160, 2, 160, 4, 64, None) == tg.TG_ERR_INVALID_ARG
+    torch.cuda.synchronize()
