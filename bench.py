@@ -7,6 +7,11 @@ workload: the 8192×14336×4096 linear-layer shape with A ~ N(0,1) and
 B ~ N(0,1/K), seeded and synthetic, resident in HBM before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+                    [--dtype f16|bf16|mxf8]
+
+--dtype bf16 times tg_gemm_bf16 on the same draws; --dtype mxf8 times the
+block-scaled FP8 entry point tg_gemm_mxf8 on the same draws encoded as E4M3
+codes with one UE8M0 scale per 32 K elements (peak: the dense fp8 rate).
 
 Prints ONE JSON line on stdout.  Timing: W untimed calls, a device
 synchronize, then K calls bracketed by HIP events recorded on the stream the
@@ -31,7 +36,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (the block-scaled entry point)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = [os.path.join(ROOT, "dense_fp16_gemm_02_amd", "csrc", f)
                   for f in ("tg_gemm.hip", "tile_layout.hpp")]
@@ -140,6 +146,8 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
     import workloads
 
     dev = torch.device("cuda:0")
+    if dtype == "mxf8":
+        return _time_mx(w, steps, warmup, rotate)
     a, b = workloads.make_inputs(w, dtype=dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     A0 = torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
@@ -184,11 +192,60 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
     return dict(ms=ms, wall_s=wall, kernel=kname, tiles=tiles, a=a, b=b)
 
 
+def _time_mx(w, steps: int, warmup: int, rotate: int):
+    """time_workload for the block-scaled FP8 entry point."""
+    import torch
+
+    import dense_fp16_gemm_02_amd as tg
+    import workloads
+
+    if w.K % 32:
+        raise RuntimeError(f"{w.name}: K = {w.K} is not whole 32-element scale blocks")
+    dev = torch.device("cuda:0")
+    qa, sa, qb, sb = workloads.make_mx_inputs(w)
+    host = [torch.from_numpy(x) for x in (qa, sa, qb, sb)]
+    sets = []
+    for r in range(rotate):
+        sets.append(tuple(x.to(dev) for x in host) + (torch.empty((w.M, w.N), dtype=torch.float16, device=dev),))
+    stream = torch.cuda.current_stream(dev)
+    nb = w.K // 32
+    st, kname, tiles = tg.tg_gemm_mxf8_plan(*sets[0], w.M, w.N, w.K, w.K, nb, w.K, nb, w.N)
+    if st != tg.TG_OK:
+        raise RuntimeError(tg.tg_status_string(st))
+
+    def step(i):
+        s = tg.tg_gemm_mxf8(*sets[i % rotate], w.M, w.N, w.K, w.K, nb, w.K, nb, w.N, stream)
+        if s != tg.TG_OK:
+            raise RuntimeError(f"tg_gemm_mxf8: {tg.tg_status_string(s)}")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    del sets
+    torch.cuda.empty_cache()
+    return dict(ms=ms, wall_s=wall, kernel=kname, tiles=tiles, a=(qa, sa), b=(qb, sb))
+
+
 def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16"):
     """Time the oracle on the first R rows of D (all N columns, full K)."""
     import numpy as np
 
     import oracle
+
+    def ref(rows, threads):
+        if fmt == "mxf8":
+            return oracle.gemm_mx(a[0], a[1], b[0], b[1], w.M, w.N, w.K, rows=rows, nthreads=threads)
+        return oracle.gemm(a, b, w.M, w.N, w.K, rows=rows, nthreads=threads, fmt=fmt)
 
     threads = oracle.default_threads()
     if rows_override:
@@ -196,13 +253,13 @@ def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16"):
     else:
         probe = min(max(1, threads), w.M)
         t0 = time.perf_counter()
-        oracle.gemm(a, b, w.M, w.N, w.K, rows=np.arange(probe), nthreads=threads, fmt=fmt)
+        ref(np.arange(probe), threads)
         per_row = (time.perf_counter() - t0) / probe
         R = int(min(w.M, max(threads, seconds / max(per_row, 1e-9))))
         R = max(threads, (R // threads) * threads) if R >= threads else R
     rows = np.arange(R, dtype=np.int64)
     t0 = time.perf_counter()
-    oracle.gemm(a, b, w.M, w.N, w.K, rows=rows, nthreads=threads, fmt=fmt)
+    ref(rows, threads)
     t = time.perf_counter() - t0
     flop = 2.0 * R * w.N * w.K
     return {
@@ -227,8 +284,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and print a table on stderr")
-    ap.add_argument("--dtype", choices=["f16", "bf16"], default="f16",
-                    help="element type (the headline metric is fp16; bf16 is reported alongside)")
+    ap.add_argument("--dtype", choices=["f16", "bf16", "mxf8"], default="f16",
+                    help="element type (the headline metric is fp16; bf16 and block-scaled FP8 "
+                         "are reported alongside)")
     ap.add_argument("--vendor", action="store_true",
                     help="with --all: also time torch.matmul on the same inputs (context)")
     ap.add_argument("--copy-bytes", type=int, default=None,
@@ -263,14 +321,18 @@ def main() -> int:
     w = workloads.BY_NAME[args.workload]
 
     if args.all:
+        pk = PEAK_FP8_TFLOPS if args.dtype == "mxf8" else PEAK_FP16_TFLOPS
         log(f"{'workload':28s} {'kernel':32s} {'us':>9s} {'TFLOP/s':>9s} {'%peak':>7s} {'GB/s':>8s}")
         for ww in workloads.WORKLOADS:
+            if args.dtype == "mxf8" and ww.K % 32:
+                log(f"{ww.name:28s} (skipped: K is not whole 32-element scale blocks)")
+                continue
             r = time_workload(ww, args.steps, args.warmup, dtype=args.dtype)
             tf = ww.flop / (r["ms"] * 1e-3) / 1e12
             gbs = ww.min_bytes / (r["ms"] * 1e-3) / 1e9
             log(f"{ww.name:28s} {r['kernel']:32s} {r['ms'] * 1e3:9.2f} {tf:9.1f} "
-                f"{100 * tf / PEAK_FP16_TFLOPS:7.2f} {gbs:8.0f}")
-            if args.vendor:
+                f"{100 * tf / pk:7.2f} {gbs:8.0f}")
+            if args.vendor and args.dtype != "mxf8":
                 v = time_workload(ww, args.steps, args.warmup, vendor=True, dtype=args.dtype)
                 tfv = ww.flop / (v["ms"] * 1e-3) / 1e12
                 log(f"{'':28s} {'torch.matmul':32s} {v['ms'] * 1e3:9.2f} {tfv:9.1f} "
@@ -279,8 +341,9 @@ def main() -> int:
     r = time_workload(w, args.steps, args.warmup, dtype=args.dtype)
     ms = r["ms"]
     tflops = w.flop / (ms * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if args.dtype == "mxf8" else PEAK_FP16_TFLOPS
     log(f"{w.name}: {r['kernel']} tiles={r['tiles']} {ms * 1e3:.2f} us/launch "
-        f"{tflops:.1f} TFLOP/s ({100 * tflops / PEAK_FP16_TFLOPS:.1f}% of peak)")
+        f"{tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of peak)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -288,10 +351,28 @@ def main() -> int:
         log(f"cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
     traffic = measured_traffic(r["kernel"], w.name)
+    shape = f"{w.M}x{w.N}x{w.K}"
+    metric = {
+        "f16": f"TFLOP/s fp16 GEMM D=A·B^T at {shape}; % of MFMA dense fp16 peak",
+        "bf16": f"TFLOP/s bf16 GEMM D=A·B^T at {shape}; % of MFMA dense bf16 peak",
+        "mxf8": f"TFLOP/s block-scaled FP8 GEMM D=(SA·A)·(SB·B)^T (E4M3, UE8M0 per 32 K) at {shape}; "
+                f"% of MFMA dense fp8 peak",
+    }[args.dtype]
+    # a contraction below the ridge point is bounded by HBM, not the matrix cores
+    elem_bytes = 1 if args.dtype == "mxf8" else 2
+    alg_bytes = elem_bytes * (w.M * w.K + w.N * w.K) + 2 * w.M * w.N
+    if args.dtype == "mxf8":
+        alg_bytes += (w.M + w.N) * (w.K // 32)  # one scale byte per 32 K elements of each row
+    hbm_bound = w.flop / alg_bytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4), "traffic": traffic}
     line = {
-        "metric": ("TFLOP/s fp16 GEMM D=A·B^T at 8192x14336x4096; % of MFMA dense fp16 peak"
-                   if args.dtype == "f16" else
-                   "TFLOP/s bf16 GEMM D=A·B^T at 8192x14336x4096; % of MFMA dense bf16 peak"),
+        "metric": metric,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -304,10 +385,8 @@ def main() -> int:
         "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "kernel": r["kernel"],
-                   "tiles": r["tiles"], "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
-                     "traffic": traffic},
+                   "tiles": r["tiles"], "pct_of_peak": round(100 * tflops / peak, 2)},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
