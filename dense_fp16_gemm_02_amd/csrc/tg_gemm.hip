@@ -61,6 +61,7 @@ struct Elem<__bf16> {
 
 __host__ __device__ constexpr int imin(int a, int b) { return a < b ? a : b; }
 __host__ __device__ constexpr int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+__host__ __device__ constexpr int imax(int a, int b) { return a > b ? a : b; }
 
 constexpr int BK = 64;              // K elements per LDS stage (128 bytes of fp16)
 constexpr int ROW_CHUNKS = BK / 8;  // 16-byte chunks per tile row
@@ -1048,6 +1049,19 @@ constexpr bool mx_fragment_covers_k_step()
 }
 static_assert(mx_fragment_covers_k_step(), "scaled-MFMA fragment reads must cover the K-step once");
 
+// Scale words of MX_GROUP = 2 consecutive K-tiles, loaded by one buffer load.
+constexpr int MX_GROUP = 2;
+template <int G>
+struct MxGroup;
+template <>
+struct MxGroup<2> {
+    typedef unsigned type __attribute__((ext_vector_type(2)));
+    __device__ static type load(__amdgpu_buffer_rsrc_t r, int off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    }
+};
+
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
@@ -1086,19 +1100,21 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     const int wm = wave / WN, wn = wave % WN;
 
     const int dr = lane / T::RC, dpc = lane % T::RC;
+    // Successive passes of a wave are NW·ROWS_PER_DMA = 32 rows apart, a
+    // whole number of swizzle periods, so a lane fetches the same logical
+    // chunk in every pass.
+    static_assert((NW * T::ROWS_PER_DMA / T::ROWS_PER_LINE) % T::RC == 0, "swizzle repeats per pass");
+    const int kc = dpc ^ T::swz(T::ROWS_PER_DMA * wave + dr);
     uint32_t a_off[A_PASSES], b_off[B_PASSES];
-    int a_kc[A_PASSES], b_kc[B_PASSES];
 #pragma unroll
     for (int p = 0; p < A_PASSES; ++p) {
         const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
-        a_kc[p] = dpc ^ T::swz(t);
-        a_off[p] = (uint32_t)(imin(t, M - 1 - m0) * lda + 16 * a_kc[p]);
+        a_off[p] = (uint32_t)(imin(t, M - 1 - m0) * lda + 16 * kc);
     }
 #pragma unroll
     for (int p = 0; p < B_PASSES; ++p) {
         const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
-        b_kc[p] = dpc ^ T::swz(t);
-        b_off[p] = (uint32_t)(imin(t, N - 1 - n0) * ldb + 16 * b_kc[p]);
+        b_off[p] = (uint32_t)(imin(t, N - 1 - n0) * ldb + 16 * kc);
     }
     const uint8_t *a_tile = A + (int64_t)m0 * lda;
     const uint8_t *b_tile = B + (int64_t)n0 * ldb;
@@ -1128,11 +1144,11 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     };
     auto dma_a = [&](const Op &o, int p) {
         dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BKB,
-                           16 * a_kc[p] < o.klim ? a_off[p] : DMA_OOB);
+                           16 * kc < o.klim ? a_off[p] : DMA_OOB);
     };
     auto dma_b = [&](const Op &o, int p) {
         dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BKB,
-                           16 * b_kc[p] < o.klim ? b_off[p] : DMA_OOB);
+                           16 * kc < o.klim ? b_off[p] : DMA_OOB);
     };
 
     // Scale words: a buffer over the rows from m0 (n0) on, so rows past M
@@ -1144,16 +1160,38 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     const __amdgpu_buffer_rsrc_t sb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(SB + (int64_t)n0 * ldsb), (short)0, (int)imin64((int64_t)(N - n0) * ldsb, DMA_RANGE),
         BUFFER_RSRC_WORD3);
-    const uint32_t sa_off = (uint32_t)((wm * WTM + srow) * ldsa), sb_off = (uint32_t)((wn * WTN + srow) * ldsb);
     const uint32_t sa_step = (uint32_t)(32 * ldsa), sb_step = (uint32_t)(32 * ldsb);
-    uint32_t sw_a[2][TM], sw_b[2][TN];  // scale words: [current, next K-tile]
-    auto load_scales = [&](int t, uint32_t *wa, uint32_t *wb) {
+    uint32_t sw_a[1][TM] = {}, sw_b[1][TN] = {};  // scale words of the current K-tile
+    // Grouped scale words: one MX_GROUP·4-byte load per lane per fragment
+    // pair covers MX_GROUP
+    // K-tiles — lanes 0..31 take row r of the pair's first fragment, lanes
+    // 32..63 row r of its second — so each load touches one cache line per
+    // row for MX_GROUP K-tiles instead of one per K-tile; a swap of the two
+    // lane halves (v_permlane32_swap) then hands every lane its own
+    // fragment's word.
+    constexpr int NPA = TM / 2, NPB = TN / 2;
+    const uint32_t sa_poff = (uint32_t)((wm * WTM + (lane >> 5) * 32 + srow) * ldsa);
+    const uint32_t sb_poff = (uint32_t)((wn * WTN + (lane >> 5) * 32 + srow) * ldsb);
+    using GroupWord = typename MxGroup<MX_GROUP>::type;
+    GroupWord gw[2][NPA + NPB] = {};  // [current, next group][pair]
+    auto load_group = [&](int t0, GroupWord *g) {
 #pragma unroll
-        for (int q = 0; q < TM; ++q)
-            wa[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(sa_rsrc, (int)(sa_off + q * sa_step + 4 * t), 0, 0);
+        for (int p = 0; p < NPA; ++p)
+            g[p] = MxGroup<MX_GROUP>::load(sa_rsrc, (int)(sa_poff + 2 * p * sa_step + 4 * t0));
 #pragma unroll
-        for (int q = 0; q < TN; ++q)
-            wb[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(sb_rsrc, (int)(sb_off + q * sb_step + 4 * t), 0, 0);
+        for (int p = 0; p < NPB; ++p)
+            g[NPA + p] = MxGroup<MX_GROUP>::load(sb_rsrc, (int)(sb_poff + 2 * p * sb_step + 4 * t0));
+    };
+    // words of K-tile j of group g into sw_a[0] / sw_b[0]
+    auto unpack_group = [&](const GroupWord *g, int j) {
+#pragma unroll
+        for (int p = 0; p < NPA + NPB; ++p) {
+            const uint32_t v = (uint32_t)g[p][j];
+            const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            uint32_t *dst = p < NPA ? &sw_a[0][2 * p] : &sw_b[0][2 * (p - NPA)];
+            dst[0] = r[0];
+            dst[1] = r[1];
+        }
     };
     // scale register for K-step kk of K-tile t from its word: block 4t+2kk+h
     auto scale_of = [&](uint32_t w, int t, int kk) {
@@ -1213,9 +1251,18 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
         }
     };
 
-    // prologue: scale words of K-tile 0, then A(0), B(0), A(1), B(1)
-    if (KT > 0)
-        load_scales(0, sw_a[0], sw_b[0]);
+    // The K loop runs over KTP = KT rounded up to an even count (at least
+    // two) in pairs of K-tiles; a K-tile past KT reads zero operands and
+    // gets unit scales (its blocks lie past K/32), so it adds nothing.
+    // Scale-word group i holds K-tiles 2i and 2i+1.  For odd KT the last
+    // group's second word lies past the last K-tile: past the end of a
+    // scale row it reads the next row's bytes, or, past the buffer, zero —
+    // the buffer unit checks each dword of a multi-dword load on its own
+    // (probed), so the first word of a straddling load is intact.
+    static_assert(MX_GROUP == 2, "the loop below pairs K-tiles");
+    const int KTP = KT < 2 ? 2 : (KT + 1) & ~1;
+    load_group(0, gw[0]);
+    // prologue DMAs: A(0), B(0), A(1), B(1)
     {
         const Op a0 = op_a(0), b0 = op_b(0), a1 = op_a(1), b1 = op_b(1);
 #pragma unroll
@@ -1233,6 +1280,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     }
     wait_vmem<A_PASSES + B_PASSES>();
     barrier_lds();
+    unpack_group(gw[0], 0);
 #pragma unroll
     for (int q = 0; q < NFRAG; ++q) {
         read_frag(0, 0, 0, q, 0, fa[0], fb[0]);
@@ -1240,27 +1288,36 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     }
 
     int sa = 0, sb = 0;
-    for (int kt = 0; kt < KT - 1; ++kt) {
-        load_scales(kt + 1, sw_a[1], sw_b[1]);
-        const Op an = op_a(kt + 2);
-        step(fa[0], fb[0], sw_a[0], sw_b[0], kt, 0, true, sa, sb, 1, fa[1], fb[1], &an, true, A_PASSES);
-        wait_vmem<A_PASSES>();  // B(kt+1), A(kt+1) and the scale words of kt+1 have landed
+    // K-tile t (t < KT-1): K-step 0 with A(t+2); wait and barrier; `extra`
+    // (the next group's loads, which then have until the following K-tile's
+    // wait to land); K-step 1 with B(t+2) and the first fragments of t+1;
+    // `after` (unpack the scale words of t+1).
+    auto k_tile = [&](int t, auto extra, auto after) __attribute__((always_inline)) {
+        const Op an = op_a(t + 2);
+        step(fa[0], fb[0], sw_a[0], sw_b[0], t, 0, true, sa, sb, 1, fa[1], fb[1], &an, true, A_PASSES);
+        wait_vmem<A_PASSES>();  // B(t+1), A(t+1) and the scale loads before them have landed
         barrier_lds();
-        const Op b2 = op_b(kt + 2);
+        extra();
+        const Op b2 = op_b(t + 2);
         const int sa1 = sa + 1 == SA_ ? 0 : sa + 1, sb1 = sb + 1 == SB_ ? 0 : sb + 1;
-        step(fa[1], fb[1], sw_a[0], sw_b[0], kt, 1, true, sa1, sb1, 0, fa[0], fb[0], &b2, false, B_PASSES);
+        step(fa[1], fb[1], sw_a[0], sw_b[0], t, 1, true, sa1, sb1, 0, fa[0], fb[0], &b2, false, B_PASSES);
         sa = sa1;
         sb = sb1;
+        after();
+    };
+    auto nothing = [] {};
+    // Pairs (kt, kt+1): the first loads group kt/2 + 1 (the last pair
+    // reloads a group in range; its words go unused).  The last K-tile runs
+    // like the others: its trailing DMAs are past K (no memory access) and
+    // its trailing fragment reads are never used.
+    for (int kt = 0; kt < KTP; kt += 2) {
+        k_tile(kt, [&] { load_group(imax(0, imin(kt + 2, KT - 1)), gw[1]); }, [&] { unpack_group(gw[0], 1); });
+        k_tile(kt + 1, nothing, [&] {
 #pragma unroll
-        for (int q = 0; q < TM; ++q)
-            sw_a[0][q] = sw_a[1][q];
-#pragma unroll
-        for (int q = 0; q < TN; ++q)
-            sw_b[0][q] = sw_b[1][q];
-    }
-    if (KT > 0) {
-        step(fa[0], fb[0], sw_a[0], sw_b[0], KT - 1, 0, true, sa, sb, 1, fa[1], fb[1], nullptr, false, 0);
-        step(fa[1], fb[1], sw_a[0], sw_b[0], KT - 1, 1, false, 0, 0, 0, fa[0], fb[0], nullptr, false, 0);
+            for (int p = 0; p < NPA + NPB; ++p)
+                gw[0][p] = gw[1][p];
+            unpack_group(gw[0], 0);
+        });
     }
     wait_vmem<0>();
 
