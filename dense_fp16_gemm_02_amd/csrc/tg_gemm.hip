@@ -1049,8 +1049,7 @@ constexpr bool mx_fragment_covers_k_step()
 }
 static_assert(mx_fragment_covers_k_step(), "scaled-MFMA fragment reads must cover the K-step once");
 
-// Scale words of MX_GROUP = 2 consecutive K-tiles, loaded by one buffer load.
-constexpr int MX_GROUP = 2;
+// Scale words of G consecutive K-tiles, loaded by one buffer load.
 template <int G>
 struct MxGroup;
 template <>
@@ -1061,8 +1060,16 @@ struct MxGroup<2> {
         return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     }
 };
+template <>
+struct MxGroup<4> {
+    typedef unsigned type __attribute__((ext_vector_type(4)));
+    __device__ static type load(__amdgpu_buffer_rsrc_t r, int off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    }
+};
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int MX_GROUP>
 __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ SB, _Float16 *__restrict__ D, int M, int N, int K, int64_t lda,
@@ -1163,12 +1170,12 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     const uint32_t sa_step = (uint32_t)(32 * ldsa), sb_step = (uint32_t)(32 * ldsb);
     uint32_t sw_a[1][TM] = {}, sw_b[1][TN] = {};  // scale words of the current K-tile
     // Grouped scale words: one MX_GROUP·4-byte load per lane per fragment
-    // pair covers MX_GROUP
-    // K-tiles — lanes 0..31 take row r of the pair's first fragment, lanes
-    // 32..63 row r of its second — so each load touches one cache line per
-    // row for MX_GROUP K-tiles instead of one per K-tile; a swap of the two
-    // lane halves (v_permlane32_swap) then hands every lane its own
-    // fragment's word.
+    // pair covers MX_GROUP K-tiles — lanes 0..31 take row r of the pair's
+    // first fragment, lanes 32..63 row r of its second — so each load
+    // touches one cache line per row for MX_GROUP K-tiles instead of one
+    // per K-tile (scattered 4-byte loads cost the address unit per line);
+    // a swap of the two lane halves (v_permlane32_swap) then hands every
+    // lane its own fragment's word.
     constexpr int NPA = TM / 2, NPB = TN / 2;
     const uint32_t sa_poff = (uint32_t)((wm * WTM + (lane >> 5) * 32 + srow) * ldsa);
     const uint32_t sb_poff = (uint32_t)((wn * WTN + (lane >> 5) * 32 + srow) * ldsb);
@@ -1251,16 +1258,16 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
         }
     };
 
-    // The K loop runs over KTP = KT rounded up to an even count (at least
-    // two) in pairs of K-tiles; a K-tile past KT reads zero operands and
-    // gets unit scales (its blocks lie past K/32), so it adds nothing.
-    // Scale-word group i holds K-tiles 2i and 2i+1.  For odd KT the last
-    // group's second word lies past the last K-tile: past the end of a
-    // scale row it reads the next row's bytes, or, past the buffer, zero —
-    // the buffer unit checks each dword of a multi-dword load on its own
-    // (probed), so the first word of a straddling load is intact.
-    static_assert(MX_GROUP == 2, "the loop below pairs K-tiles");
-    const int KTP = KT < 2 ? 2 : (KT + 1) & ~1;
+    // The K loop runs over KTP = KT rounded up to a multiple of MX_GROUP (at
+    // least one group) in groups of K-tiles; a K-tile past KT reads zero
+    // operands and gets unit scales (its blocks lie past K/32), so it adds
+    // nothing.  Scale-word group i holds K-tiles G·i .. G·i+G-1.  Where KT is
+    // not a multiple of G the last group's words past the last K-tile lie
+    // past the end of a scale row: they read the next row's bytes or, past
+    // the buffer, zero — the buffer unit checks each dword of a multi-dword
+    // load on its own (probed), so the group's words in range are intact.
+    static_assert(MX_GROUP == 2 || MX_GROUP == 4, "groups of two or four K-tiles");
+    const int KTP = KT < MX_GROUP ? MX_GROUP : (KT + MX_GROUP - 1) / MX_GROUP * MX_GROUP;
     load_group(0, gw[0]);
     // prologue DMAs: A(0), B(0), A(1), B(1)
     {
@@ -1306,13 +1313,16 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
         after();
     };
     auto nothing = [] {};
-    // Pairs (kt, kt+1): the first loads group kt/2 + 1 (the last pair
-    // reloads a group in range; its words go unused).  The last K-tile runs
-    // like the others: its trailing DMAs are past K (no memory access) and
-    // its trailing fragment reads are never used.
-    for (int kt = 0; kt < KTP; kt += 2) {
-        k_tile(kt, [&] { load_group(imax(0, imin(kt + 2, KT - 1)), gw[1]); }, [&] { unpack_group(gw[0], 1); });
-        k_tile(kt + 1, nothing, [&] {
+    // Group (kt .. kt+G-1): its first K-tile loads the next group (the last
+    // group reloads one in range; its words go unused).  The last K-tile
+    // runs like the others: its trailing DMAs are past K (no memory access)
+    // and its trailing fragment reads are never used.
+    for (int kt = 0; kt < KTP; kt += MX_GROUP) {
+        k_tile(kt, [&] { load_group(imax(0, imin(kt + MX_GROUP, KT - 1)), gw[1]); }, [&] { unpack_group(gw[0], 1); });
+#pragma unroll
+        for (int j = 1; j + 1 < MX_GROUP; ++j)
+            k_tile(kt + j, nothing, [&] { unpack_group(gw[0], j + 1); });
+        k_tile(kt + MX_GROUP - 1, nothing, [&] {
 #pragma unroll
             for (int p = 0; p < NPA + NPB; ++p)
                 gw[0][p] = gw[1][p];
@@ -1654,8 +1664,12 @@ extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const 
     int dvec = (ldd % 8 == 0) && ((uintptr_t)D % 16 == 0);
     void *args[] = {(void *)&A, (void *)&SA, (void *)&B, (void *)&SB, (void *)&D, &Mi, &Ni, &Ki,
                     &lda, &ldsa, &ldb, &ldsb, &ldd, &tiles_m, &tiles_n, &dvec};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2>),
-                                   dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
+    // groups of four K-tiles when they divide the K-tile count, else pairs
+    // (at most one padding K-tile)
+    const int64_t kt = (K + 127) / 128;
+    const void *fn = kt % 4 == 0 ? reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 4>)
+                                 : reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 2>);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
