@@ -203,18 +203,20 @@ def _time_mx(w, steps: int, warmup: int, rotate: int):
         raise RuntimeError(f"{w.name}: K = {w.K} is not whole 32-element scale blocks")
     dev = torch.device("cuda:0")
     qa, sa, qb, sb = workloads.make_mx_inputs(w)
-    host = [torch.from_numpy(x) for x in (qa, sa, qb, sb)]
+    nb = w.K // 32
+    lds = (nb + 3) // 4 * 4  # scale rows padded to whole 4-byte words (the entry point's rule)
+    host = [torch.from_numpy(x) for x in (qa, workloads.pad_bytes(sa, lds, 127), qb,
+                                          workloads.pad_bytes(sb, lds, 127))]
     sets = []
     for r in range(rotate):
         sets.append(tuple(x.to(dev) for x in host) + (torch.empty((w.M, w.N), dtype=torch.float16, device=dev),))
     stream = torch.cuda.current_stream(dev)
-    nb = w.K // 32
-    st, kname, tiles = tg.tg_gemm_mxf8_plan(*sets[0], w.M, w.N, w.K, w.K, nb, w.K, nb, w.N)
+    st, kname, tiles = tg.tg_gemm_mxf8_plan(*sets[0], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N)
     if st != tg.TG_OK:
         raise RuntimeError(tg.tg_status_string(st))
 
     def step(i):
-        s = tg.tg_gemm_mxf8(*sets[i % rotate], w.M, w.N, w.K, w.K, nb, w.K, nb, w.N, stream)
+        s = tg.tg_gemm_mxf8(*sets[i % rotate], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N, stream)
         if s != tg.TG_OK:
             raise RuntimeError(f"tg_gemm_mxf8: {tg.tg_status_string(s)}")
 
