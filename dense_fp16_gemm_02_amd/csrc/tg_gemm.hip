@@ -774,8 +774,9 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
 //   K-step 2: A(t+2), second half      wait until all but A(t+2) landed
 //   barrier (A stage t mod 3 and B stage t mod 2 are drained)
 //   K-step 3: B(t+2), first half (and the fragments of K-tile t+1, step 0)
-// Everything else (swizzle, fragment reads, tails, staged epilogue) is as in
-// gemm_dma_kernel; rows past M or N are clamped.
+// Everything else (swizzle, fragment reads, staged epilogue) is as in
+// gemm_dma_kernel; rows past M or N are clamped, and a K that is not a
+// multiple of 64 makes the first K-tile (not the last) the partial one.
 template <typename E, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_kernel(
     const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
@@ -830,51 +831,68 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
     const char *a_tile = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
     const char *b_tile = reinterpret_cast<const char *>(B + (int64_t)n0 * ldb);
     const int KT = (K + BK_ - 1) / BK_;
+    // K-tile t covers columns k0 + 64t .. k0 + 64t + 63 with k0 = K - 64·KT
+    // (<= 0): only the first K-tile can be partial, and its columns below 0
+    // read as zero (those lanes get an offset past the range), so the DMAs
+    // of the K loop carry no per-lane bounds test (a vector select per DMA
+    // costs the matrix core issue cycles); K-tiles past the last get an
+    // empty buffer range, where every lane reads zero.
+    const int k0 = K - BK_ * KT;
 
     // DMA source and LDS stage of one operand's K-tile
     struct Op {
         __amdgpu_buffer_rsrc_t r;
         E *dst;
-        int klim;  // valid K elements (0 past the end)
     };
     auto op_a = [&](int t) {
-        const int k = t * BK_;
         Op o;
-        o.r = __builtin_amdgcn_make_buffer_rsrc((void *)(a_tile + 2 * k), (short)0, DMA_RANGE,
-                                                BUFFER_RSRC_WORD3);
+        o.r = __builtin_amdgcn_make_buffer_rsrc((void *)(a_tile + 2 * (int64_t)(k0 + t * BK_)), (short)0,
+                                                t < KT ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
         o.dst = a_ring + (t % SA) * STAGE_A;
-        o.klim = t < KT ? K - k : 0;
         return o;
     };
     auto op_b = [&](int t) {
-        const int k = t * BK_;
         Op o;
-        o.r = __builtin_amdgcn_make_buffer_rsrc((void *)(b_tile + 2 * k), (short)0, DMA_RANGE,
-                                                BUFFER_RSRC_WORD3);
+        o.r = __builtin_amdgcn_make_buffer_rsrc((void *)(b_tile + 2 * (int64_t)(k0 + t * BK_)), (short)0,
+                                                t < KT ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
         o.dst = b_ring + (t % SB) * STAGE_B;
-        o.klim = t < KT ? K - k : 0;
         return o;
     };
     auto dma_a = [&](const Op &o, int p) {
-        dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BK_,
-                           8 * a_kc[p] < o.klim ? a_off[p] : DMA_OOB);
+        dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BK_, a_off[p]);
     };
     auto dma_b = [&](const Op &o, int p) {
+        dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BK_, b_off[p]);
+    };
+    // K-tile 0: lanes whose chunk lies below column 0 read zero
+    auto dma_a0 = [&](const Op &o, int p) {
         dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BK_,
-                           8 * b_kc[p] < o.klim ? b_off[p] : DMA_OOB);
+                           k0 + 8 * a_kc[p] >= 0 ? a_off[p] : DMA_OOB);
+    };
+    auto dma_b0 = [&](const Op &o, int p) {
+        dma16<CPOL_CACHED>(o.r, o.dst + (p * NW + wave) * T::ROWS_PER_DMA * BK_,
+                           k0 + 8 * b_kc[p] >= 0 ? b_off[p] : DMA_OOB);
     };
 
     const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
     V8 fa[2][TM], fb[2][TN];
+    // The swizzle repeats every 16 rows, so a lane's chunk position in
+    // K-step kk is the same for every fragment: one per-lane offset per
+    // K-step, and fragment q sits a constant 32 rows further (an immediate
+    // offset of the LDS read, no address arithmetic per read).
+    static_assert(T::swz(16) == T::swz(0) && WTM % 16 == 0 && WTN % 16 == 0, "swizzle period");
+    int a_lane[KSTEPS], b_lane[KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+        a_lane[kk] = T::off(wm * WTM + frag_row, kk * 2 + frag_hi);
+        b_lane[kk] = T::off(wn * WTN + frag_row, kk * 2 + frag_hi);
+    }
     // fragment q of K-step kk of the K-tile in A stage sa / B stage sb
     auto read_frag = [&](int sa, int sb, int kk, int q, V8 *a, V8 *b) {
-        const int c = kk * 2 + frag_hi;
         if (q < TM)
-            a[q] = *reinterpret_cast<const V8 *>(a_ring + sa * STAGE_A +
-                                                    T::off(wm * WTM + q * 32 + frag_row, c));
+            a[q] = *reinterpret_cast<const V8 *>(a_ring + sa * STAGE_A + a_lane[kk] + q * 32 * BK_);
         else
-            b[q - TM] = *reinterpret_cast<const V8 *>(
-                b_ring + sb * STAGE_B + T::off(wn * WTN + (q - TM) * 32 + frag_row, c));
+            b[q - TM] = *reinterpret_cast<const V8 *>(b_ring + sb * STAGE_B + b_lane[kk] + (q - TM) * 32 * BK_);
     };
 
     f32x16 acc[TM][TN];
@@ -932,10 +950,10 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
         const Op a0 = op_a(0), b0 = op_b(0), a1 = op_a(1), b1 = op_b(1);
 #pragma unroll
         for (int p = 0; p < A_PASSES; ++p)
-            dma_a(a0, p);
+            dma_a0(a0, p);
 #pragma unroll
         for (int p = 0; p < B_PASSES; ++p)
-            dma_b(b0, p);
+            dma_b0(b0, p);
 #pragma unroll
         for (int p = 0; p < A_PASSES; ++p)
             dma_a(a1, p);
