@@ -1208,27 +1208,41 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
             g[NPA + p] = MxGroup<MX_GROUP>::load(sb_rsrc, (int)(sb_poff + 2 * p * sb_step + 4 * t0));
     };
     // words of K-tile j of group g into sw_a[0] / sw_b[0]
-    auto unpack_group = [&](const GroupWord *g, int j) {
+    // Words of K-tile t (index j of group g) into sw_a[0] / sw_b[0], ready
+    // for the MFMA: blocks at or past K/32 (the tail of a partial last
+    // K-tile, and K-tiles past the end) become 2^0 by a wave-uniform byte
+    // mask, and each lane shifts its word right by 8·h, so that byte 2·kk
+    // (the MFMA's byte select for K-step kk) holds block 4t + 2kk + h.
+    auto unpack_group = [&](const GroupWord *g, int j, int t) {
+        const int nv = nblk - 4 * t;
+        const uint32_t keep = nv >= 4 ? 0xffffffffu : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
+        const uint32_t unit = 0x7f7f7f7fu & ~keep;
+        const uint32_t sh = 8 * shalf;
 #pragma unroll
         for (int p = 0; p < NPA + NPB; ++p) {
-            const uint32_t v = (uint32_t)g[p][j];
+            const uint32_t v = ((uint32_t)g[p][j] & keep) | unit;
             const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
             uint32_t *dst = p < NPA ? &sw_a[0][2 * p] : &sw_b[0][2 * (p - NPA)];
-            dst[0] = r[0];
-            dst[1] = r[1];
+            dst[0] = r[0] >> sh;
+            dst[1] = r[1] >> sh;
         }
-    };
-    // scale register for K-step kk of K-tile t from its word: block 4t+2kk+h
-    auto scale_of = [&](uint32_t w, int t, int kk) {
-        const int blk = 4 * t + 2 * kk + shalf;
-        return blk < nblk ? (int)(w >> (16 * kk + 8 * shalf)) : 127;
     };
 
     i32x8 fa[2][TM], fb[2][TN];
+    // per-lane byte offsets of chunk (kk, half) in a stage; the swizzle
+    // repeats every 16 rows, so fragment q sits a constant q·32 rows further
+    static_assert(T::swz(16) == T::swz(0) && WTM % 16 == 0 && WTN % 16 == 0, "swizzle period");
+    int a_lane[KSTEPS][2], b_lane[KSTEPS][2];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            a_lane[kk][half] = 2 * T::off(wm * WTM + srow, mx_chunk_of(lane, kk, half));
+            b_lane[kk][half] = 2 * T::off(wn * WTN + srow, mx_chunk_of(lane, kk, half));
+        }
     auto read_frag = [&](int sa, int sb, int kk, int q, int half, i32x8 *a, i32x8 *b) {
-        const int c = mx_chunk_of(lane, kk, half);
-        const uint8_t *src = q < TM ? a_ring + sa * STAGE_A + 2 * T::off(wm * WTM + q * 32 + srow, c)
-                                    : b_ring + sb * STAGE_B + 2 * T::off(wn * WTN + (q - TM) * 32 + srow, c);
+        const uint8_t *src = q < TM ? a_ring + sa * STAGE_A + a_lane[kk][half] + q * 32 * BKB
+                                    : b_ring + sb * STAGE_B + b_lane[kk][half] + (q - TM) * 32 * BKB;
         const i32x4 v = *reinterpret_cast<const i32x4 *>(src);
         i32x8 &f = q < TM ? a[q] : b[q - TM];
 #pragma unroll
@@ -1251,18 +1265,17 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     auto step = [&](const i32x8 *a, const i32x8 *b, const uint32_t *wa, const uint32_t *wb, int t, int kk,
                     bool with_reads, int rsa, int rsb, int rkk, i32x8 *na, i32x8 *nb, const Op *o, bool is_a,
                     int n) {
-        int sa_reg[TM], sb_reg[TN];
-#pragma unroll
-        for (int q = 0; q < TM; ++q)
-            sa_reg[q] = scale_of(wa[q], t, kk);
-#pragma unroll
-        for (int q = 0; q < TN; ++q)
-            sb_reg[q] = scale_of(wb[q], t, kk);
+        (void)t;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const int ti = i / TN, tj = i % TN;
-            acc[ti][tj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[tj], a[ti], acc[ti][tj], 0, 0, 0,
-                                                                          sb_reg[tj], 0, sa_reg[ti]);
+            // the scale byte of K-step kk is byte 2·kk of the prepared word
+            if (kk == 0)
+                acc[ti][tj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    b[tj], a[ti], acc[ti][tj], 0, 0, 0, (int)wb[tj], 0, (int)wa[ti]);
+            else
+                acc[ti][tj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    b[tj], a[ti], acc[ti][tj], 0, 0, 2, (int)wb[tj], 2, (int)wa[ti]);
             MFMA_FIRST();
             if (with_reads)
                 read_frag(rsa, rsb, rkk, frag_of_slot(i / 2), i % 2, na, nb);
@@ -1305,7 +1318,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     }
     wait_vmem<A_PASSES + B_PASSES>();
     barrier_lds();
-    unpack_group(gw[0], 0);
+    unpack_group(gw[0], 0, 0);
 #pragma unroll
     for (int q = 0; q < NFRAG; ++q) {
         read_frag(0, 0, 0, q, 0, fa[0], fb[0]);
@@ -1336,15 +1349,16 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     // runs like the others: its trailing DMAs are past K (no memory access)
     // and its trailing fragment reads are never used.
     for (int kt = 0; kt < KTP; kt += MX_GROUP) {
-        k_tile(kt, [&] { load_group(imax(0, imin(kt + MX_GROUP, KT - 1)), gw[1]); }, [&] { unpack_group(gw[0], 1); });
+        k_tile(kt, [&] { load_group(imax(0, imin(kt + MX_GROUP, KT - 1)), gw[1]); },
+               [&] { unpack_group(gw[0], 1, kt + 1); });
 #pragma unroll
         for (int j = 1; j + 1 < MX_GROUP; ++j)
-            k_tile(kt + j, nothing, [&] { unpack_group(gw[0], j + 1); });
+            k_tile(kt + j, nothing, [&] { unpack_group(gw[0], j + 1, kt + j + 1); });
         k_tile(kt + MX_GROUP - 1, nothing, [&] {
 #pragma unroll
             for (int p = 0; p < NPA + NPB; ++p)
                 gw[0][p] = gw[1][p];
-            unpack_group(gw[0], 0);
+            unpack_group(gw[0], 0, kt + MX_GROUP);
         });
     }
     wait_vmem<0>();
