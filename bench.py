@@ -274,6 +274,15 @@ def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16"):
     }
 
 
+def algorithmic_bytes(w, dtype: str) -> int:
+    """Compulsory HBM bytes of one call: A and B read once, D (fp16) written once;
+    the block-scaled entry point reads 1-byte codes plus one scale byte per 32 K
+    elements of each row."""
+    if dtype == "mxf8":
+        return (w.M * w.K + w.N * w.K) + 2 * w.M * w.N + (w.M + w.N) * (w.K // 32)
+    return w.min_bytes
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,7 +340,7 @@ def main() -> int:
                 continue
             r = time_workload(ww, args.steps, args.warmup, dtype=args.dtype)
             tf = ww.flop / (r["ms"] * 1e-3) / 1e12
-            gbs = ww.min_bytes / (r["ms"] * 1e-3) / 1e9
+            gbs = algorithmic_bytes(ww, args.dtype) / (r["ms"] * 1e-3) / 1e9
             log(f"{ww.name:28s} {r['kernel']:32s} {r['ms'] * 1e3:9.2f} {tf:9.1f} "
                 f"{100 * tf / pk:7.2f} {gbs:8.0f}")
             if args.vendor and args.dtype != "mxf8":
@@ -361,10 +370,7 @@ def main() -> int:
                 f"% of MFMA dense fp8 peak",
     }[args.dtype]
     # a contraction below the ridge point is bounded by HBM, not the matrix cores
-    elem_bytes = 1 if args.dtype == "mxf8" else 2
-    alg_bytes = elem_bytes * (w.M * w.K + w.N * w.K) + 2 * w.M * w.N
-    if args.dtype == "mxf8":
-        alg_bytes += (w.M + w.N) * (w.K // 32)  # one scale byte per 32 K elements of each row
+    alg_bytes = algorithmic_bytes(w, args.dtype)
     hbm_bound = w.flop / alg_bytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if hbm_bound:
         gbs = alg_bytes / (ms * 1e-3) / 1e9
