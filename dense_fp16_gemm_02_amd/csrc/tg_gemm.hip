@@ -31,6 +31,7 @@
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Element type of A, B and D: binary16 or bfloat16.  Both take the same
 // tiles, DMAs and LDS layouts (2-byte elements); they differ only in the
@@ -47,6 +48,10 @@ struct Elem<_Float16> {
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
+    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
 };
 template <>
 struct Elem<__bf16> {
@@ -56,6 +61,10 @@ struct Elem<__bf16> {
     __device__ static f32x16 mfma(v8 a, v8 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
 
@@ -94,6 +103,19 @@ static_assert(tg::layout::check_operand_fragment(frag_row_of, frag_hi_of),
               "operand fragment reads disagree with the MFMA operand layout");
 static_assert(tg::layout::check_acc_fragment(acc_row_of, acc_col_of),
               "epilogue disagrees with the MFMA accumulator layout");
+
+// The same for v_mfma_f32_16x16x32_f16: lane l takes row (l & 15) and
+// K-chunk (l >> 4) of a 16×32 operand slice; register v of lane l is D row
+// (l & 15), D column 4·(l >> 4) + v of a 16×16 tile.
+__host__ __device__ constexpr int frag16_row_of(int l) { return l & 15; }
+__host__ __device__ constexpr int frag16_hi_of(int l) { return l >> 4; }
+__host__ __device__ constexpr int acc16_row_of(int l, int) { return l & 15; }
+__host__ __device__ constexpr int acc16_col_of(int l, int v) { return 4 * (l >> 4) + v; }
+static_assert(tg::layout::check_operand_fragment(frag16_row_of, frag16_hi_of,
+                                                 tg::layout::mfma16x16x32_operand(), 32),
+              "operand fragment reads disagree with the 16x16x32 MFMA operand layout");
+static_assert(tg::layout::check_acc_fragment(acc16_row_of, acc16_col_of, tg::layout::mfma16x16_acc_swapped(), 16),
+              "epilogue map disagrees with the 16x16 MFMA accumulator layout");
 
 // Workgroup id → output tile.  The hardware hands workgroup w to XCD w mod 8;
 // each XCD gets a contiguous range of logical tile ids, and logical ids walk
@@ -769,15 +791,27 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
 // MFMAs included.  The third A stage gives A's refill two K-tiles, so each of
 // the four K-steps now carries four DMAs per wave: B's refill in the last
 // K-step of a tile and the first of the next (same latency budget as before),
-// A's refill, one K-tile further ahead, in the next two.  Per iteration t:
+// A's refill, one K-tile further ahead, in the next two.  Per iteration t
+// with MF = 32 (four 16-K steps of 32×32×16 MFMAs):
 //   K-step 0: B(t+1), second half      K-step 1: A(t+2), first half
 //   K-step 2: A(t+2), second half      wait until all but A(t+2) landed
 //   barrier (A stage t mod 3 and B stage t mod 2 are drained)
 //   K-step 3: B(t+2), first half (and the fragments of K-tile t+1, step 0)
-// Everything else (swizzle, fragment reads, staged epilogue) is as in
+// With MF = 16 (two 32-K steps of 64 16×16×32 MFMAs each) K-step 0 carries
+// all of A(t+2), then the wait and the barrier, and K-step 1 all of B(t+2),
+// one DMA every eighth MFMA.  Everything else (swizzle, fragment reads, staged epilogue) is as in
 // gemm_dma_kernel; rows past M or N are clamped, and a K that is not a
 // multiple of 64 makes the first K-tile (not the last) the partial one.
-template <typename E, int BM, int BN, int WM, int WN>
+template <int MF>
+struct AccOf {
+    typedef f32x16 type;  // 32×32 MFMA: 16 fp32 per lane
+};
+template <>
+struct AccOf<16> {
+    typedef f32x4 type;  // 16×16 MFMA: 4 fp32 per lane
+};
+
+template <typename E, int BM, int BN, int WM, int WN, int MF>
 __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_kernel(
     const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
@@ -789,13 +823,18 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
     using T = OperandTile<BK_>;
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int KSTEPS = BK_ / 16;
+    using Acc = typename AccOf<MF>::type;
+    constexpr int TM = WTM / MF, TN = WTN / MF;
+    constexpr int KW = MF == 32 ? 16 : 32;  // K per MFMA
+    constexpr int KSTEPS = BK_ / KW;
+    constexpr int CPK = KW / 8;  // 16-byte chunks per row per K-step
+    constexpr int ACC_REGS = MF * MF / 64;
     constexpr int A_PASSES = BM / T::ROWS_PER_DMA / NW, B_PASSES = BN / T::ROWS_PER_DMA / NW;
     constexpr int AH = A_PASSES / 2, BH = B_PASSES / 2;
     constexpr int STAGE_A = BM * BK_, STAGE_B = BN * BK_;
-    static_assert(KSTEPS == 4 && A_PASSES % 2 == 0 && B_PASSES % 2 == 0, "schedule assumes 4 K-steps");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(MF == 32 || MF == 16, "32×32×16 or 16×16×32 MFMA");
+    static_assert(A_PASSES % 2 == 0 && B_PASSES % 2 == 0, "DMA passes split in halves");
+    static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
     static_assert((BM / T::ROWS_PER_DMA) % NW == 0 && (BN / T::ROWS_PER_DMA) % NW == 0,
                   "DMA row groups must split evenly over the waves");
     static_assert((SA * STAGE_A + SB * STAGE_B) * 2 <= 160 * 1024, "LDS budget");
@@ -874,7 +913,8 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
                            k0 + 8 * b_kc[p] >= 0 ? b_off[p] : DMA_OOB);
     };
 
-    const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
+    const int frag_row = MF == 32 ? frag_row_of(lane) : frag16_row_of(lane);
+    const int frag_hi = MF == 32 ? frag_hi_of(lane) : frag16_hi_of(lane);
     V8 fa[2][TM], fb[2][TN];
     // The swizzle repeats every 16 rows, so a lane's chunk position in
     // K-step kk is the same for every fragment: one per-lane offset per
@@ -884,31 +924,32 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
     int a_lane[KSTEPS], b_lane[KSTEPS];
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-        a_lane[kk] = T::off(wm * WTM + frag_row, kk * 2 + frag_hi);
-        b_lane[kk] = T::off(wn * WTN + frag_row, kk * 2 + frag_hi);
+        a_lane[kk] = T::off(wm * WTM + frag_row, kk * CPK + frag_hi);
+        b_lane[kk] = T::off(wn * WTN + frag_row, kk * CPK + frag_hi);
     }
     // fragment q of K-step kk of the K-tile in A stage sa / B stage sb
     auto read_frag = [&](int sa, int sb, int kk, int q, V8 *a, V8 *b) {
         if (q < TM)
-            a[q] = *reinterpret_cast<const V8 *>(a_ring + sa * STAGE_A + a_lane[kk] + q * 32 * BK_);
+            a[q] = *reinterpret_cast<const V8 *>(a_ring + sa * STAGE_A + a_lane[kk] + q * MF * BK_);
         else
-            b[q - TM] = *reinterpret_cast<const V8 *>(b_ring + sb * STAGE_B + b_lane[kk] + (q - TM) * 32 * BK_);
+            b[q - TM] = *reinterpret_cast<const V8 *>(b_ring + sb * STAGE_B + b_lane[kk] + (q - TM) * MF * BK_);
     };
 
-    f32x16 acc[TM][TN];
+    Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
+            for (int v = 0; v < ACC_REGS; ++v)
                 acc[i][j][v] = 0.0f;
 
     constexpr int NFRAG = TM + TN;
     constexpr int SLOTS = TM * TN;
     // fragment reads every other slot, DMAs in the odd slots between them:
     // the LDS sees reads and DMA writes interleaved rather than in bursts
-    constexpr int RSTRIDE = 2;
+    constexpr int RSTRIDE = SLOTS / NFRAG;
+    static_assert(RSTRIDE >= 2 && RSTRIDE % 2 == 0, "reads go in even slots");
     auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
     // One K-step: MFMA per slot; the next step's read i after MFMA i (i <
     // NFRAG); the DMA passes [lo, hi) of `o` (A when is_a) from slot 1 at an
@@ -945,6 +986,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
             }
     };
 
+    if constexpr (KSTEPS == 4) {
     // prologue: A(0), B(0), A(1), first half of B(1); wait for A(0) and B(0)
     {
         const Op a0 = op_a(0), b0 = op_b(0), a1 = op_a(1), b1 = op_b(1);
@@ -987,6 +1029,51 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
         step(fa[0], fb[0], true, sa, sb, 3, fa[1], fb[1], nullptr, false, 0, 0);
         step(fa[1], fb[1], false, 0, 0, 0, fa[0], fb[0], nullptr, false, 0, 0);
     }
+    } else {
+        // Two K-steps per K-tile (16×16×32): K-step 0 carries A(t+2), the
+        // wait and barrier follow, and K-step 1 carries B(t+2) while it reads
+        // the first K-step of tile t+1.  B(t+2) lands in B stage t mod 2,
+        // drained at this barrier; A(t+2) in A stage (t-1) mod 3, drained at
+        // the previous one.  The prologue issues A(0), B(0), A(1), B(1).
+        {
+            const Op a0 = op_a(0), b0 = op_b(0), a1 = op_a(1), b1 = op_b(1);
+#pragma unroll
+            for (int p = 0; p < A_PASSES; ++p)
+                dma_a0(a0, p);
+#pragma unroll
+            for (int p = 0; p < B_PASSES; ++p)
+                dma_b0(b0, p);
+#pragma unroll
+            for (int p = 0; p < A_PASSES; ++p)
+                dma_a(a1, p);
+#pragma unroll
+            for (int p = 0; p < B_PASSES; ++p)
+                dma_b(b1, p);
+        }
+        wait_vmem<A_PASSES + B_PASSES>();
+        barrier_lds();
+#pragma unroll
+        for (int q = 0; q < NFRAG; ++q)
+            read_frag(0, 0, 0, q, fa[0], fb[0]);
+
+        int sa = 0, sb = 0;
+        for (int kt = 0; kt < KT - 1; ++kt) {
+            const Op an = op_a(kt + 2);
+            step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], &an, true, 0, A_PASSES);
+            wait_vmem<A_PASSES>();  // B(kt+1) and A(kt+1) have landed; A(kt+2) may not
+            barrier_lds();
+            const Op b2 = op_b(kt + 2);
+            const int sa1 = sa + 1 == SA ? 0 : sa + 1, sb1 = sb + 1 == SB ? 0 : sb + 1;
+            step(fa[1], fb[1], true, sa1, sb1, 0, fa[0], fb[0], &b2, false, 0, B_PASSES);
+            sa = sa1;
+            sb = sb1;
+        }
+        // the last K-tile; with K = 0 every DMA above had an empty range, so
+        // the stages hold zeros and this adds nothing (no branch here: a
+        // conditional tail made the register allocator rotate accumulators)
+        step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], nullptr, false, 0, 0);
+        step(fa[1], fb[1], false, 0, 0, 0, fa[0], fb[0], nullptr, false, 0, 0);
+    }
     wait_vmem<0>();  // no LDS DMA may be outstanding when the wave ends
 
     // staged epilogue, as in gemm_dma_kernel
@@ -1002,13 +1089,14 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g = 0; g < ACC_REGS / 4; ++g) {
                 V4 h;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     h[r] = (E)acc[i][j][g * 4 + r];  // round to nearest even
-                const int r = i * 32 + frag_row;
-                const int c = j * 32 + g * 8 + frag_hi * 4;
+                // four consecutive D columns of row r
+                const int r = i * MF + frag_row;
+                const int c = j * MF + (MF == 32 ? g * 8 + frag_hi * 4 : frag_hi * 4);
                 *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
             }
     store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
@@ -1425,6 +1513,13 @@ struct KernelChoice {
 #define TG_M_KROT 0
 #endif
 
+// MFMA shape of the 256×256 kernel: 16 (v_mfma_f32_16x16x32, the default:
+// the same work in twice the instructions draws less power, so the clock
+// holds higher under load) or 32 (v_mfma_f32_32x32x16).
+#ifndef TG_L_MF
+#define TG_L_MF 16
+#endif
+
 // Load path of a launch: direct-to-LDS DMA, 16-byte loads through registers
 // (aligned operands whose in-tile offsets exceed 32 bits), or element-wise.
 enum LoadPath { PATH_DMA = 0, PATH_VEC = 1, PATH_SCALAR = 2 };
@@ -1540,7 +1635,7 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     if (tiles(256, 256) >= NUM_CU) {
         const LoadPath lp = path(256, 256);
         if (lp == PATH_DMA)
-            k = {reinterpret_cast<const void *>(&gemm_dma3_kernel<E, 256, 256, 2, 2>), TILE_256, 256,
+            k = {reinterpret_cast<const void *>(&gemm_dma3_kernel<E, 256, 256, 2, 2, TG_L_MF>), TILE_256, 256,
                  256, 256, PATH_DMA};
         else
             k = choice<E, 256, 256, 2, 2, 64, 2>(lp, TILE_256);

@@ -274,6 +274,26 @@ constexpr TileLayout mfma32x32_acc_swapped()
     return t;
 }
 
+// Operand fragment of v_mfma_f32_16x16x32_f16 over a logical 16×32 (row, k)
+// tile: lane = row + 16·(k / 8), register element = k mod 8, i.e.
+// S[(16,4,8):(1@laneid,16@laneid,1@m)].
+constexpr TileLayout mfma16x16x32_operand()
+{
+    TileLayout t;
+    t.S(16, 1, laneid).S(4, 16, laneid).S(8, 1, m);
+    return t;
+}
+
+// Accumulator of v_mfma_f32_16x16x32_f16 with the inputs swapped, over a
+// logical 16×16 tile of D: D row = lane % 16, D col = 4·(lane/16) + v, i.e.
+// S[(16,4,4):(1@laneid,16@laneid,1@m)].
+constexpr TileLayout mfma16x16_acc_swapped()
+{
+    TileLayout t;
+    t.S(16, 1, laneid).S(4, 16, laneid).S(4, 1, m);
+    return t;
+}
+
 // ------------------------------------------------------------- checks
 
 // The kernels' LDS chunk address fn(r, c) (element offset of 16-byte chunk c
@@ -291,36 +311,38 @@ constexpr bool check_swizzled_tile(const ComposeLayout &L, int rows, int cols, F
     return true;
 }
 
-// A fragment read by lane l, element e, of chunk 2·kk + hi(l) of row row(l)
-// matches mfma32x32x16_operand for every (row, k) of the 32×16 tile.
+// A fragment read by lane l, element e, of chunk (K-step base) + hi(l) of row
+// row(l) matches the operand layout L of a rows × kw MFMA slice for every
+// (row, k): by default v_mfma_f32_32x32x16_f16's 32×16 slice.
 template <class RowF, class HiF>
-constexpr bool check_operand_fragment(RowF row_of_lane, HiF hi_of_lane)
+constexpr bool check_operand_fragment(RowF row_of_lane, HiF hi_of_lane,
+                                      const TileLayout &L = mfma32x32x16_operand(), int kw = 16)
 {
-    const TileLayout L = mfma32x32x16_operand();
     for (int l = 0; l < 64; ++l)
         for (int e = 0; e < 8; ++e) {
             const int64_t k = hi_of_lane(l) * 8 + e;
-            const Coord c = L.apply2(row_of_lane(l), k, 16);
+            const Coord c = L.apply2(row_of_lane(l), k, kw);
             if (c[laneid] != l || c[m] != e)
                 return false;
         }
     return true;
 }
 
-// The epilogue's (lane, register) → (D row, D col) map equals
-// mfma32x32_acc_swapped, and is a bijection onto the 32×32 tile.
+// The epilogue's (lane, register) → (D row, D col) map equals the swapped
+// accumulator layout L of an mf × mf MFMA tile (by default
+// mfma32x32_acc_swapped), and is a bijection onto the tile.
 template <class RowF, class ColF>
-constexpr bool check_acc_fragment(RowF drow, ColF dcol)
+constexpr bool check_acc_fragment(RowF drow, ColF dcol, const TileLayout &L = mfma32x32_acc_swapped(),
+                                  int mf = 32)
 {
-    const TileLayout L = mfma32x32_acc_swapped();
     bool seen[32 * 32] = {};
     for (int l = 0; l < 64; ++l)
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < mf * mf / 64; ++v) {
             const int r = drow(l, v), c = dcol(l, v);
-            if (r < 0 || r >= 32 || c < 0 || c >= 32 || seen[r * 32 + c])
+            if (r < 0 || r >= mf || c < 0 || c >= mf || seen[r * mf + c])
                 return false;
-            seen[r * 32 + c] = true;
-            const Coord x = L.apply2(r, c, 32);
+            seen[r * mf + c] = true;
+            const Coord x = L.apply2(r, c, mf);
             if (x[laneid] != l || x[m] != v)
                 return false;
         }
