@@ -231,16 +231,16 @@ def test_strip_index_pattern_exact():
     assert np.array_equal(d.astype(np.int64), want)
 
 
-def test_persistent_tiles_exact():
-    """More 256×256 tiles than resident workgroups (17×17 = 289): workgroups
-    take a second tile whose first K-tiles load during the first tile's
-    epilogue.  Integer operands: every checked element is exact."""
+def test_second_wave_tiles_exact():
+    """More 256×256 tiles than compute units (17×17 = 289), so some units run
+    a second tile after the first.  Integer operands: every checked element
+    is exact."""
     M, N, K = 4352 - 5, 4352 - 3, 136
     a, b = workloads.index_pattern(M, N, K)
     st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N + 2)
-    say(f"persistent plan {name} tiles={tiles}")
+    say(f"second-wave plan {name} tiles={tiles}")
     assert name.startswith("gemm_f16_256x256_") and tiles == 289
-    d, full, st = run(a, b, M, N, K, guard=1, label="persistent exact")
+    d, full, st = run(a, b, M, N, K, guard=1, label="second-wave exact")
     assert st == tg.TG_OK and guard_intact(full, M, N, 1)
     rows = np.unique(np.concatenate([np.arange(0, 300), np.arange(M - 300, M),
                                      np.arange(2048 - 8, 2048 + 8)]))
@@ -248,18 +248,36 @@ def test_persistent_tiles_exact():
     assert np.array_equal(d[rows].astype(np.int64), want)
 
 
-def test_persistent_zero_k():
-    """K = 0 with more tiles than resident workgroups: every tile is +0."""
+def test_second_wave_zero_k():
+    """K = 0 through the 256×256 kernel with more tiles than compute units:
+    every tile is +0 (its last K-tile runs unconditionally on stages that
+    empty DMA ranges filled with zeros; the NaN operands are never read)."""
     M, N = 4352, 4352
     # lda = ldb = 8 keeps the direct-to-LDS kernel; the NaN columns are never read
     a = np.full((M, 8), np.nan, dtype=np.float16)
     b = np.full((N, 8), np.nan, dtype=np.float16)
     st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, 0, 8, 8, N + 2)
-    say(f"persistent K=0 plan {name} tiles={tiles}")
+    say(f"second-wave K=0 plan {name} tiles={tiles}")
     assert name.endswith("_dma") and tiles == 289
-    d, full, st = run(a, b, M, N, 0, guard=1, label="persistent K=0")
+    d, full, st = run(a, b, M, N, 0, guard=1, label="second-wave K=0")
     assert st == tg.TG_OK and guard_intact(full, M, N, 1)
     assert np.all(_bits(d) == 0)
+
+
+@pytest.mark.parametrize("K", [8, 64, 72, 120])
+def test_large_tile_short_k_exact(K):
+    """Short K through the 256×256 kernel: one K-tile (K = 8, 64) or two whose
+    first is the partial one (K = 72, 120); integer operands, exact."""
+    M, N = 4096 + 40, 4096 + 24
+    a, b = workloads.index_pattern(M, N, K)
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N)
+    say(f"short-K plan {name} tiles={tiles} K={K}")
+    assert name.startswith("gemm_f16_256x256_") and name.endswith("_dma")
+    d, full, st = run(a, b, M, N, K, guard=1, label=f"short-K {K}")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 1)
+    rows = np.unique(np.concatenate([np.arange(0, 260), np.arange(M - 260, M)]))
+    want = a[rows].astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(d[rows].astype(np.int64), want)
 
 
 # ------------------------------------------------------- degenerate cases
