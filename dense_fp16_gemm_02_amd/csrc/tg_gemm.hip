@@ -3,18 +3,22 @@
 //
 // Data path per workgroup (the GMEM → shared → matrix unit → register → GMEM
 // path of "TIRx 基础", section "从一个最小 GEMM 开始", re-planned for CDNA4):
-//   1. every thread loads 16-byte chunks of the A and B K-slices from global
-//      memory into registers (coalesced along K), then writes them into an
-//      XOR-swizzled LDS tile — the 128-byte swizzle of "TIRx Layout API",
-//      section "示例：对 (8, 64) float16 Tile 应用 128B Swizzle";
-//   2. two LDS stages form a ring across the K loop: while the matrix cores
-//      consume stage s, the loads for the next K-slice are in flight and land
-//      in stage s^1 ("TIRx 与高性能GEMM (上)", Step 5);
+//   1. the A and B K-slices move from global memory straight into LDS by
+//      direct-to-LDS buffer loads (16 bytes per lane, coalesced along K); the
+//      XOR swizzle of "TIRx Layout API", section "示例：对 (8, 64) float16
+//      Tile 应用 128B Swizzle", re-derived for a 64-bank LDS, is applied on
+//      the source side (operands that are not 16-byte aligned go through
+//      registers instead);
+//   2. LDS stages form rings across the K loop: while the matrix cores
+//      consume one stage, the loads of the next K-slices are in flight into
+//      the others ("TIRx 与高性能GEMM (上)", Step 5; the largest tile keeps
+//      three stages of A and two of B);
 //   3. each wave reads its operand fragments with 128-bit LDS reads and issues
-//      v_mfma_f32_32x32x16_f16 into fp32 accumulators held in registers;
-//      the first K-slice starts from zero (the pages' accum=False);
-//   4. the epilogue rounds fp32 → fp16 to nearest-even and stores only the
-//      part of the tile inside M×N.
+//      v_mfma_f32_16x16x32_f16 (largest tile) or v_mfma_f32_32x32x16_f16 into
+//      fp32 accumulators held in registers; the first K-slice starts from
+//      zero (the pages' accum=False);
+//   4. the epilogue rounds fp32 → fp16 to nearest-even, stages the tile in
+//      LDS and stores the part inside M×N in 16-byte row segments.
 // Elements beyond M, N or K are read as zero and never written, so any shape
 // works ("从编译器能力到公开算子", section "SM90a 支持具体补了什么": tail
 // copies mask the valid prefix).
