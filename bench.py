@@ -15,7 +15,11 @@ codes with one UE8M0 scale per 32 K elements (peak: the dense fp8 rate).
 
 Prints ONE JSON line on stdout.  Timing: W untimed calls, a device
 synchronize, then K calls bracketed by HIP events recorded on the stream the
-kernel is launched on (torch's current stream), then a synchronize.  Two
+kernel is launched on (torch's current stream), then a synchronize.  With
+--records R the K-call window is timed R times and the median window is
+reported (all R in records_ms_per_step); --per-call adds a separate pass of K
+calls with an event between consecutive calls and reports their median, min
+and quartiles.  Two
 operand/output sets alternate between calls so consecutive launches do not
 find their operands in the last-level cache from the previous call.
 
@@ -171,8 +175,49 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _timed(step, steps: int, warmup: int, records: int, per_call: bool, dev, stream) -> dict:
+    """W untimed calls, then `records` windows of K calls, each bracketed by
+    two HIP events on the launch stream (a window's mean is one record; the
+    default is one window, i.e. exactly K timed calls); with `per_call`, one
+    more pass of K calls with an event between consecutive calls for the
+    per-call distribution (kept out of the windows: the extra events would
+    sit between the launches being timed)."""
+    import statistics
+
+    import torch
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    means = []
+    t0 = time.perf_counter()
+    for r in range(records):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(steps):
+            step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize(dev)
+        means.append(ev0.elapsed_time(ev1) / steps)
+    wall = time.perf_counter() - t0
+    out = dict(ms=statistics.median(means), records_ms=means, wall_s=wall, per_call_us=None)
+    if per_call:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(stream)
+        for i in range(steps):
+            step(i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize(dev)
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps))
+        q = statistics.quantiles(per, n=4) if steps >= 2 else [per[0]] * 3
+        out["per_call_us"] = {"median": round(statistics.median(per), 3), "min": round(per[0], 3),
+                              "p25": round(q[0], 3), "p75": round(q[2], 3)}
+    return out
+
+
 def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = False,
-                  dtype: str = "f16"):
+                  dtype: str = "f16", records: int = 1, per_call: bool = False):
     import numpy as np
     import torch
 
@@ -181,7 +226,7 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
 
     dev = torch.device("cuda:0")
     if dtype == "mxf8":
-        return _time_mx(w, steps, warmup, rotate)
+        return _time_mx(w, steps, warmup, rotate, records, per_call)
     a, b = workloads.make_inputs(w, dtype=dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     A0 = torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
@@ -208,25 +253,13 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
         if s != tg.TG_OK:
             raise RuntimeError(f"{call.__name__}: {tg.tg_status_string(s)}")
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / steps
+    t = _timed(step, steps, warmup, records, per_call, dev, stream)
     del sets, A0, B0
     torch.cuda.empty_cache()
-    return dict(ms=ms, wall_s=wall, kernel=kname, tiles=tiles, a=a, b=b)
+    return dict(t, kernel=kname, tiles=tiles, a=a, b=b)
 
 
-def _time_mx(w, steps: int, warmup: int, rotate: int):
+def _time_mx(w, steps: int, warmup: int, rotate: int, records: int = 1, per_call: bool = False):
     """time_workload for the block-scaled FP8 entry point."""
     import torch
 
@@ -254,22 +287,10 @@ def _time_mx(w, steps: int, warmup: int, rotate: int):
         if s != tg.TG_OK:
             raise RuntimeError(f"tg_gemm_mxf8: {tg.tg_status_string(s)}")
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / steps
+    t = _timed(step, steps, warmup, records, per_call, dev, stream)
     del sets
     torch.cuda.empty_cache()
-    return dict(ms=ms, wall_s=wall, kernel=kname, tiles=tiles, a=(qa, sa), b=(qb, sb))
+    return dict(t, kernel=kname, tiles=tiles, a=(qa, sa), b=(qb, sb))
 
 
 def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16"):
@@ -322,6 +343,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--records", type=int, default=1,
+                    help="timed windows of --steps calls; the reported time is their median")
+    ap.add_argument("--per-call", action="store_true",
+                    help="also time --steps calls one by one (median, min, quartiles)")
     ap.add_argument("--workload", default="linear_8192x14336x4096")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target length of the oracle sample")
@@ -372,18 +397,24 @@ def main() -> int:
             if args.dtype == "mxf8" and ww.K % 32:
                 log(f"{ww.name:28s} (skipped: K is not whole 32-element scale blocks)")
                 continue
-            r = time_workload(ww, args.steps, args.warmup, dtype=args.dtype)
+            r = time_workload(ww, args.steps, args.warmup, dtype=args.dtype, records=max(1, args.records),
+                              per_call=args.per_call)
             tf = ww.flop / (r["ms"] * 1e-3) / 1e12
             gbs = algorithmic_bytes(ww, args.dtype) / (r["ms"] * 1e-3) / 1e9
+            pc = r["per_call_us"]
             log(f"{ww.name:28s} {r['kernel']:32s} {r['ms'] * 1e3:9.2f} {tf:9.1f} "
-                f"{100 * tf / pk:7.2f} {gbs:8.0f}")
+                f"{100 * tf / pk:7.2f} {gbs:8.0f}"
+                + (f"  per call: median {pc['median']:.2f} min {pc['min']:.2f} "
+                   f"IQR {pc['p25']:.2f}-{pc['p75']:.2f} us" if pc else ""))
             if args.vendor and args.dtype != "mxf8":
-                v = time_workload(ww, args.steps, args.warmup, vendor=True, dtype=args.dtype)
+                v = time_workload(ww, args.steps, args.warmup, vendor=True, dtype=args.dtype,
+                                  records=max(1, args.records))
                 tfv = ww.flop / (v["ms"] * 1e-3) / 1e12
                 log(f"{'':28s} {'torch.matmul':32s} {v['ms'] * 1e3:9.2f} {tfv:9.1f} "
                     f"{100 * tfv / PEAK_FP16_TFLOPS:7.2f} {ww.min_bytes / (v['ms'] * 1e-3) / 1e9:8.0f}")
 
-    r = time_workload(w, args.steps, args.warmup, dtype=args.dtype)
+    r = time_workload(w, args.steps, args.warmup, dtype=args.dtype, records=max(1, args.records),
+                      per_call=args.per_call)
     ms = r["ms"]
     tflops = w.flop / (ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if args.dtype == "mxf8" else PEAK_FP16_TFLOPS
@@ -431,6 +462,10 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if len(r["records_ms"]) > 1:
+        line["records_ms_per_step"] = [round(x, 6) for x in r["records_ms"]]
+    if r["per_call_us"]:
+        line["per_call_us"] = r["per_call_us"]
     print(json.dumps(line), flush=True)
     return 0
 
