@@ -53,8 +53,8 @@ def log(msg: str) -> None:
 
 
 def _code_text(src: str) -> str:
-    """C++ source with comments and blank lines removed, trailing spaces cut:
-    what the compiler sees, so an edit to a comment keeps a traffic record."""
+    """C++ source with comments, blank lines and indentation removed: what the
+    compiler sees, so an edit to a comment or to layout keeps a traffic record."""
     out, i, n = [], 0, len(src)
     quote = None
     while i < n:
@@ -81,7 +81,7 @@ def _code_text(src: str) -> str:
         else:
             out.append(c)
             i += 1
-    lines = (line.rstrip() for line in "".join(out).split("\n"))
+    lines = (line.strip() for line in "".join(out).split("\n"))
     return "\n".join(line for line in lines if line)
 
 

@@ -991,48 +991,48 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
     };
 
     if constexpr (KSTEPS == 4) {
-    // prologue: A(0), B(0), A(1), first half of B(1); wait for A(0) and B(0)
-    {
-        const Op a0 = op_a(0), b0 = op_b(0), a1 = op_a(1), b1 = op_b(1);
+        // prologue: A(0), B(0), A(1), first half of B(1); wait for A(0) and B(0)
+        {
+            const Op a0 = op_a(0), b0 = op_b(0), a1 = op_a(1), b1 = op_b(1);
 #pragma unroll
-        for (int p = 0; p < A_PASSES; ++p)
-            dma_a0(a0, p);
+            for (int p = 0; p < A_PASSES; ++p)
+                dma_a0(a0, p);
 #pragma unroll
-        for (int p = 0; p < B_PASSES; ++p)
-            dma_b0(b0, p);
+            for (int p = 0; p < B_PASSES; ++p)
+                dma_b0(b0, p);
 #pragma unroll
-        for (int p = 0; p < A_PASSES; ++p)
-            dma_a(a1, p);
+            for (int p = 0; p < A_PASSES; ++p)
+                dma_a(a1, p);
 #pragma unroll
-        for (int p = 0; p < BH; ++p)
-            dma_b(b1, p);
-    }
-    wait_vmem<A_PASSES + BH>();
-    barrier_lds();
+            for (int p = 0; p < BH; ++p)
+                dma_b(b1, p);
+        }
+        wait_vmem<A_PASSES + BH>();
+        barrier_lds();
 #pragma unroll
-    for (int q = 0; q < NFRAG; ++q)
-        read_frag(0, 0, 0, q, fa[0], fb[0]);
+        for (int q = 0; q < NFRAG; ++q)
+            read_frag(0, 0, 0, q, fa[0], fb[0]);
 
-    int sa = 0, sb = 0;  // stages of K-tile kt
-    for (int kt = 0; kt < KT - 1; ++kt) {
-        const Op bn = op_b(kt + 1), an = op_a(kt + 2);
-        step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], &bn, false, BH, B_PASSES);
-        step(fa[1], fb[1], true, sa, sb, 2, fa[0], fb[0], &an, true, 0, AH);
-        step(fa[0], fb[0], true, sa, sb, 3, fa[1], fb[1], &an, true, AH, A_PASSES);
-        wait_vmem<A_PASSES>();  // K-tile kt+1 has landed (this wave's part); A(kt+2) may not
-        barrier_lds();          // ... for every wave; A stage sa and B stage sb are drained
-        const Op b2 = op_b(kt + 2);
-        const int sa1 = sa + 1 == SA ? 0 : sa + 1, sb1 = sb + 1 == SB ? 0 : sb + 1;
-        step(fa[1], fb[1], true, sa1, sb1, 0, fa[0], fb[0], &b2, false, 0, BH);
-        sa = sa1;
-        sb = sb1;
-    }
-    if (KT > 0) {
-        step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], nullptr, false, 0, 0);
-        step(fa[1], fb[1], true, sa, sb, 2, fa[0], fb[0], nullptr, false, 0, 0);
-        step(fa[0], fb[0], true, sa, sb, 3, fa[1], fb[1], nullptr, false, 0, 0);
-        step(fa[1], fb[1], false, 0, 0, 0, fa[0], fb[0], nullptr, false, 0, 0);
-    }
+        int sa = 0, sb = 0;  // stages of K-tile kt
+        for (int kt = 0; kt < KT - 1; ++kt) {
+            const Op bn = op_b(kt + 1), an = op_a(kt + 2);
+            step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], &bn, false, BH, B_PASSES);
+            step(fa[1], fb[1], true, sa, sb, 2, fa[0], fb[0], &an, true, 0, AH);
+            step(fa[0], fb[0], true, sa, sb, 3, fa[1], fb[1], &an, true, AH, A_PASSES);
+            wait_vmem<A_PASSES>();  // K-tile kt+1 has landed (this wave's part); A(kt+2) may not
+            barrier_lds();          // ... for every wave; A stage sa and B stage sb are drained
+            const Op b2 = op_b(kt + 2);
+            const int sa1 = sa + 1 == SA ? 0 : sa + 1, sb1 = sb + 1 == SB ? 0 : sb + 1;
+            step(fa[1], fb[1], true, sa1, sb1, 0, fa[0], fb[0], &b2, false, 0, BH);
+            sa = sa1;
+            sb = sb1;
+        }
+        if (KT > 0) {
+            step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], nullptr, false, 0, 0);
+            step(fa[1], fb[1], true, sa, sb, 2, fa[0], fb[0], nullptr, false, 0, 0);
+            step(fa[0], fb[0], true, sa, sb, 3, fa[1], fb[1], nullptr, false, 0, 0);
+            step(fa[1], fb[1], false, 0, 0, 0, fa[0], fb[0], nullptr, false, 0, 0);
+        }
     } else {
         // Two K-steps per K-tile (16×16×32): K-step 0 carries A(t+2), the
         // wait and barrier follow, and K-step 1 carries B(t+2) while it reads
