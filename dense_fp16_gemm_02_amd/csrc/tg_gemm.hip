@@ -1481,6 +1481,228 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
 }
 
+// Column-strip variant of the block-scaled GEMM for small M (M <= 64): one
+// 64-row tile row covers all of M, so each workgroup streams its own
+// 128-row band of B exactly once (the fp16 strip tiles' argument: the shape
+// is bound by reading B from HBM, not by the matrix cores).  Four waves
+// split the band by columns (64×32 each: two 32-row A fragments, one B
+// fragment per 64-K step); STAGES LDS stages hold, per 128-K tile, A's 64
+// and B's 128 operand rows (same swizzle and source-side DMA addressing as
+// the 256×256 kernel).  The scale words ride the same DMA stream, four
+// K-tiles at a time: at the first K-tile of a group of four, one
+// 16-byte-per-lane DMA per wave (wave 0: A rows 0..63, waves 1 and 2: B
+// rows 0..63 and 64..127) fills one of three scale slots (scattered scale
+// loads cost the address unit per cache line: a DMA per K-tile cost 18% of
+// the time); at the other K-tiles, and always in wave 3, an empty DMA into
+// a spare slot keeps every wave's count of DMAs in flight the same.  B's
+// DMAs stream past the caches; the workgroups on XCD x start their K loop at
+// K-tile x·KT/8 (rounded down to a group) and wrap around, so the eight XCDs
+// read different column bands of B's rows at a time.  Each K-tile: wait for
+// its DMAs, barrier, refill the stage drained by the barrier with K-tile
+// t+STAGES-1 (K-tiles past the end get empty ranges: no memory access), then
+// the scale words (masked to 2^0 past K/32, shifted for the lane half) and
+// two 64-K steps of two MFMAs.
+template <int STAGES>
+__global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ SB, _Float16 *__restrict__ D, int M, int N, int K, int64_t lda,
+    int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd, int dvec)
+{
+    using E = _Float16;
+    using V4 = Elem<E>::v4;
+    constexpr int BM = 64, BN = 128, NW = 4, BKB = 128;
+    constexpr int WTM = BM, WTN = BN / NW;       // 64×32 per wave
+    constexpr int TM = WTM / 32, TN = WTN / 32;  // 2 A fragments, 1 B fragment
+    using T = OperandTile<64>;                   // 128-byte rows; T::off counts 2-byte units
+    constexpr int A_PASSES = BM / T::ROWS_PER_DMA / NW, B_PASSES = BN / T::ROWS_PER_DMA / NW;
+    constexpr int DPT = A_PASSES + B_PASSES + 1;  // DMAs per K-tile per wave (the last: scale words)
+    constexpr int STAGE_A = BM * BKB, STAGE_B = BN * BKB;  // bytes
+    constexpr int STAGE = STAGE_A + STAGE_B;
+    constexpr int SC_SLOT = 16 * 64 * NW;  // scale words of 4 K-tiles: 16 bytes per lane and wave
+    static_assert(STAGES >= 2 && STAGES <= 5, "a scale slot is rewritten 3 groups later");
+    static_assert(STAGES * STAGE + 4 * SC_SLOT <= 160 * 1024, "LDS budget");
+    static_assert((STAGES - 1) * DPT <= 63, "vmcnt holds 6 bits");
+    static_assert(NW * WTM * WTN * 2 <= STAGES * STAGE, "staging fits in the stage memory");
+    static_assert((BM / T::ROWS_PER_DMA) % NW == 0 && (BN / T::ROWS_PER_DMA) % NW == 0,
+                  "DMA row groups must split evenly over the waves");
+    static_assert(T::swz(16) == T::swz(0) && WTN % 16 == 0, "swizzle period");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + 4 * SC_SLOT];
+    uint8_t *const sc_ring = smem + STAGES * STAGE;  // three slots, then one that empty DMAs fill
+
+    const int n0 = blockIdx.x * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int dr = lane / T::RC, dpc = lane % T::RC;
+    uint32_t a_off[A_PASSES], b_off[B_PASSES];
+    int a_kc[A_PASSES], b_kc[B_PASSES];
+#pragma unroll
+    for (int p = 0; p < A_PASSES; ++p) {
+        const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
+        a_kc[p] = dpc ^ T::swz(t);
+        a_off[p] = (uint32_t)(imin(t, M - 1) * lda + 16 * a_kc[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < B_PASSES; ++p) {
+        const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
+        b_kc[p] = dpc ^ T::swz(t);
+        b_off[p] = (uint32_t)(imin(t, N - 1 - n0) * ldb + 16 * b_kc[p]);
+    }
+    const uint8_t *b_band = B + (int64_t)n0 * ldb;
+    // scale rows from row 0 of A and row n0 of B; rows past M (N) read zero
+    // words (they feed only unstored outputs)
+    const __amdgpu_buffer_rsrc_t sc_rsrc =
+        wave == 0 ? __builtin_amdgcn_make_buffer_rsrc((void *)SA, (short)0,
+                                                      (int)imin64((int64_t)M * ldsa, DMA_RANGE), BUFFER_RSRC_WORD3)
+                  : __builtin_amdgcn_make_buffer_rsrc((void *)(SB + (int64_t)n0 * ldsb), (short)0,
+                                                      (int)imin64((int64_t)(N - n0) * ldsb, DMA_RANGE),
+                                                      BUFFER_RSRC_WORD3);
+    const uint32_t sc_off = wave == 0 ? (uint32_t)(lane * ldsa) : (uint32_t)(((wave - 1) * 64 + lane) * ldsb);
+
+    const int KT = (K + BKB - 1) / BKB;
+    const int nblk = K / 32;
+    // a multiple of 4, so that the K-tiles of each group of four are visited
+    // together (the group holding the last K-tile may be shorter)
+    const int kstart = KT > 0 ? ((int)(blockIdx.x % 8) * KT / 8) & ~3 : 0;
+    // K-tile index of loop step t (steps past KT are empty)
+    auto ktile = [&](int t) { return t < KT ? (t + kstart) % KT : t; };
+    // scale slot of loop step t: groups in visiting order, modulo 3 (a slot
+    // is refilled STAGES-1 <= 4 steps before its group's first step, by
+    // which time the group three back has been read: at most one group, the
+    // one that ends at the last K-tile, is shorter than four)
+    const int before_wrap = KT - kstart;
+    auto slot = [&](int t) {
+        const int g = t < before_wrap ? t / 4 : (before_wrap + 3) / 4 + (t - before_wrap) / 4;
+        return g % 3;
+    };
+    auto issue = [&](int t) {
+        const int kt = ktile(t);
+        const bool live = t < KT;
+        uint8_t *st = smem + (t % STAGES) * STAGE;
+        const int klim = live ? K - kt * BKB : 0;  // valid bytes of each row in this K-tile
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(A + (int64_t)kt * BKB), (short)0, live ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(b_band + (int64_t)kt * BKB), (short)0, live ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
+#pragma unroll
+        for (int p = 0; p < A_PASSES; ++p)
+            dma16<CPOL_CACHED>(ra, st + (p * NW + wave) * T::ROWS_PER_DMA * BKB,
+                               16 * a_kc[p] < klim ? a_off[p] : DMA_OOB);
+#pragma unroll
+        for (int p = 0; p < B_PASSES; ++p)
+            dma16<CPOL_STREAM>(rb, st + STAGE_A + (p * NW + wave) * T::ROWS_PER_DMA * BKB,
+                               16 * b_kc[p] < klim ? b_off[p] : DMA_OOB);
+        // at a group's first K-tile, 16 bytes per row: its four words (words
+        // past the row's last K-tile are never used); otherwise an empty DMA
+        // into the spare slot keeps the count
+        const bool first = live && wave < 3 && kt % 4 == 0;
+        dma16<CPOL_CACHED>(sc_rsrc, sc_ring + (first ? slot(t) : 3) * SC_SLOT + wave * 1024,
+                           first ? sc_off + 4 * kt : DMA_OOB);
+    };
+
+    const int srow = mx_row_of(lane), shalf = lane >> 5;
+    int a_lane[2][2], b_lane[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            a_lane[kk][half] = 2 * T::off(srow, mx_chunk_of(lane, kk, half));
+            b_lane[kk][half] = STAGE_A + 2 * T::off(wave * WTN + srow, mx_chunk_of(lane, kk, half));
+        }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[i][j][v] = 0.0f;
+
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t)
+        issue(t);
+    for (int t = 0; t < KT; ++t) {
+        wait_vmem<(STAGES - 2) * DPT>();  // this wave's DMAs of K-tile t have landed
+        barrier_lds();                    // ... every wave's; the stage of t-1 is drained
+        issue(t + STAGES - 1);
+        const uint8_t *st = smem + (t % STAGES) * STAGE;
+        // scale words: blocks at or past K/32 become 2^0 (the operand bytes
+        // there are zero, the padding's scale bytes may be anything); lane
+        // r + 32·h shifts by 8·h so that byte 2·kk holds block 4·kt + 2·kk + h
+        const int nv = nblk - 4 * ktile(t);
+        const uint32_t keep = nv >= 4 ? 0xffffffffu : (1u << (8 * nv)) - 1u;
+        const uint32_t unit = 0x7f7f7f7fu & ~keep;
+        // word kt mod 4 of row r sits at byte 16·r + 4·(kt mod 4) of the slot
+        // (B's rows after A's 64)
+        const uint32_t *sw = reinterpret_cast<const uint32_t *>(sc_ring + slot(t) * SC_SLOT) + ktile(t) % 4;
+        uint32_t wa[TM], wb[TN];
+#pragma unroll
+        for (int q = 0; q < TM; ++q)
+            wa[q] = ((sw[4 * (q * 32 + srow)] & keep) | unit) >> (8 * shalf);
+#pragma unroll
+        for (int q = 0; q < TN; ++q)
+            wb[q] = ((sw[4 * (64 + wave * WTN + q * 32 + srow)] & keep) | unit) >> (8 * shalf);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            i32x8 fa[TM], fb[TN];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                for (int q = 0; q < TM; ++q) {
+                    const i32x4 v = *reinterpret_cast<const i32x4 *>(st + a_lane[kk][half] + q * 32 * BKB);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        fa[q][4 * half + e] = v[e];
+                }
+#pragma unroll
+                for (int q = 0; q < TN; ++q) {
+                    const i32x4 v = *reinterpret_cast<const i32x4 *>(st + b_lane[kk][half] + q * 32 * BKB);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        fb[q][4 * half + e] = v[e];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    if (kk == 0)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fb[j], fa[i], acc[i][j], 0, 0, 0, (int)wb[j], 0, (int)wa[i]);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fb[j], fa[i], acc[i][j], 0, 0, 2, (int)wb[j], 2, (int)wa[i]);
+                }
+        }
+    }
+    wait_vmem<0>();  // the trailing empty DMAs still write their stages
+    barrier_lds();   // every wave is done with the stages before they hold D
+
+    // staged epilogue, as in gemm_dma_kernel
+    constexpr int SROW = WTN;
+    constexpr int SCH = WTN / 8;
+    static_assert((SCH & (SCH - 1)) == 0 && SCH >= 2, "chunk swizzle needs a power of two");
+    auto stage_off = [](int r, int chunk) { return r * SROW + ((chunk ^ (r & (SCH - 1))) << 3); };
+    E *stg = reinterpret_cast<E *>(smem) + wave * WTM * WTN;
+    const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                V4 h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    h[r] = (E)acc[i][j][g * 4 + r];  // round to nearest even
+                const int r = i * 32 + frag_row;
+                const int c = j * 32 + g * 8 + frag_hi * 4;
+                *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
+            }
+    store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, 0, n0 + wave * WTN, M, N, dvec, lane);
+}
+
 struct KernelChoice {
     const void *fn;
     const char *tile;  // "<BM>x<BN>_w<WM>x<WN>"
@@ -1754,8 +1976,14 @@ extern "C" int tg_gemm_bf16_plan(const void *A, const void *B, const void *D, in
 }
 
 // Block-scaled FP8 entry point: argument checks, then one 256×256 tile per
-// workgroup.
+// workgroup, or for M <= 64 and N of at least 128 column strips one 64×128
+// strip per workgroup.
 constexpr const char *MXF8_KERNEL = "gemm_mxf8_256x256_w2x2_dma";
+constexpr const char *MXF8_STRIP_KERNEL = "gemm_mxf8_64x128_w1x4_dma";
+#ifndef TG_MX_STRIP_STAGES
+#define TG_MX_STRIP_STAGES 4
+#endif
+bool mx_uses_strip(int64_t M, int64_t N) { return M <= 64 && (N + 127) / 128 >= NUM_CU / 2; }
 
 int validate_mx(const void *A, const void *SA, const void *B, const void *SB, const void *D, int64_t M,
                 int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd)
@@ -1787,12 +2015,20 @@ extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const 
     st = check_device();
     if (st != TG_OK)
         return st;
+    int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+    int dvec = (ldd % 8 == 0) && ((uintptr_t)D % 16 == 0);
+    if (mx_uses_strip(M, N)) {
+        void *sargs[] = {(void *)&A, (void *)&SA, (void *)&B, (void *)&SB, (void *)&D, &Mi, &Ni, &Ki,
+                         &lda, &ldsa, &ldb, &ldsb, &ldd, &dvec};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemm_mxf8_strip_kernel<TG_MX_STRIP_STAGES>),
+                                       dim3((unsigned)((N + 127) / 128)), dim3(256), sargs, 0,
+                                       (hipStream_t)stream);
+        return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+    }
     int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
     const int64_t grid = (int64_t)tiles_m * tiles_n;
     if (grid >= LIMIT32)
         return TG_ERR_TOO_LARGE;
-    int Mi = (int)M, Ni = (int)N, Ki = (int)K;
-    int dvec = (ldd % 8 == 0) && ((uintptr_t)D % 16 == 0);
     void *args[] = {(void *)&A, (void *)&SA, (void *)&B, (void *)&SB, (void *)&D, &Mi, &Ni, &Ki,
                     &lda, &ldsa, &ldb, &ldsb, &ldd, &tiles_m, &tiles_n, &dvec};
     // groups of four K-tiles when they divide the K-tile count, else pairs
@@ -1816,10 +2052,11 @@ extern "C" int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, c
         *tiles = 0;
     if (st != TG_OK || M == 0 || N == 0)
         return st;
+    const bool strip = mx_uses_strip(M, N);
     if (name && name_len > 0)
-        snprintf(name, (size_t)name_len, "%s", MXF8_KERNEL);
+        snprintf(name, (size_t)name_len, "%s", strip ? MXF8_STRIP_KERNEL : MXF8_KERNEL);
     if (tiles)
-        *tiles = ((M + 255) / 256) * ((N + 255) / 256);
+        *tiles = strip ? (N + 127) / 128 : ((M + 255) / 256) * ((N + 255) / 256);
     return TG_OK;
 }
 

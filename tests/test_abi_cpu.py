@@ -142,8 +142,19 @@ def test_mxf8_plans_and_validation():
         if w.K % 32:
             assert st == tg.TG_ERR_LAYOUT and name == "" and tiles == 0
             continue
-        assert st == tg.TG_OK and name == "gemm_mxf8_256x256_w2x2_dma"
-        assert tiles == ((w.M + 255) // 256) * ((w.N + 255) // 256)
+        if w.M <= 64 and (w.N + 127) // 128 >= 128:  # column strips for small M
+            assert st == tg.TG_OK and name == "gemm_mxf8_64x128_w1x4_dma"
+            assert tiles == (w.N + 127) // 128
+        else:
+            assert st == tg.TG_OK and name == "gemm_mxf8_256x256_w2x2_dma"
+            assert tiles == ((w.M + 255) // 256) * ((w.N + 255) // 256)
+    # the strip needs M <= 64 and at least 128 strips
+    assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 16384, 128, 128, 4, 128, 4, 16384)[1] == \
+        "gemm_mxf8_64x128_w1x4_dma"
+    assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 16384, 128, 128, 4, 128, 4, 16384)[1] == \
+        "gemm_mxf8_256x256_w2x2_dma"
+    assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 16256, 128, 128, 4, 128, 4, 16256)[1] == \
+        "gemm_mxf8_256x256_w2x2_dma"
     ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 128, 128, 4, 128, 4, 64)
     assert tg.tg_gemm_mxf8_plan(*ok)[0] == tg.TG_OK
 

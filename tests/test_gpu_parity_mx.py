@@ -178,6 +178,84 @@ def test_partial_k_tiles_and_nan_padding(K):
     assert _guard_ok(full, M, N, 2)
 
 
+STRIP = "gemm_mxf8_64x128_w1x4_dma"
+
+
+def _plan_name(M, N, K, lda, ldsa, ldb, ldsb, ldd):
+    st, name, tiles = tg.tg_gemm_mxf8_plan(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+                                           M, N, K, lda, ldsa, ldb, ldsb, ldd)
+    assert st == tg.TG_OK
+    return name
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 16400, 1024), (37, 16411, 224), (1, 16385, 32), (64, 16384, 4096 + 96)])
+def test_strip_every_element(M, N, K):
+    """Small M takes the column-strip kernel (each XCD starts at its own
+    K-tile and wraps around); every element against the oracle, NaN scale
+    bytes in the scale-row padding, a guard band around D."""
+    qa, sa = workloads.random_mx(41 + K, M, K, 118, 124)
+    qb, sb = workloads.random_mx(42 + K, N, K, 118, 124)
+    nb = K // 32
+    sa_p, sb_p = _padded_scales(sa, _ld4(nb) + 4), _padded_scales(sb, _ld4(nb))
+    assert _plan_name(M, N, K, K, sa_p.shape[1], K, sb_p.shape[1], N + 4) == STRIP
+    res = oracle.gemm_mx(qa, sa, qb, sb, M, N, K)
+    d, full, st = run_mx(qa, sa_p, qb, sb_p, M, N, K, guard=2, label="strip")
+    assert st == tg.TG_OK
+    _check(d, res, f"strip {M}x{N}x{K}")
+    assert _guard_ok(full, M, N, 2)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 16500, 384), (50, 16390, 96)])
+def test_strip_random_scales_exact(M, N, K):
+    """±1/0 operands with scales 2^-3..2^3 through the strip kernel: bit-exact."""
+    a, b = _pm1(51 + K, M, K), _pm1(52 + K, N, K)
+    rng = np.random.default_rng(53 + K)
+    nb = K // 32
+    sa = _padded_scales(rng.integers(124, 131, size=(M, nb)).astype(np.uint8), _ld4(nb))
+    sb = _padded_scales(rng.integers(124, 131, size=(N, nb)).astype(np.uint8), _ld4(nb))
+    assert _plan_name(M, N, K, K, sa.shape[1], K, sb.shape[1], N) == STRIP
+    res = oracle.gemm_mx(a, sa, b, sb, M, N, K)
+    d, _, st = run_mx(a, sa, b, sb, M, N, K, label="strip random scales")
+    assert st == tg.TG_OK
+    assert np.array_equal(d.view(np.uint16), res.d.view(np.uint16))
+
+
+@pytest.mark.parametrize("side", ["a", "b"])
+def test_strip_block_scale_lands_on_its_block(side):
+    """The block probes on the strip kernel: one block of one row raised to 2^3
+    moves exactly that row (column) of D by 7·32."""
+    M, N, K = 64, 16400, 224   # two K-tiles, the second partial
+    nb = K // 32
+    ones_a = np.full((M, K), ONE, np.uint8)
+    ones_b = np.full((N, K), ONE, np.uint8)
+    for probe, (row, blk) in enumerate([(0, 0), (33, 3), (63 if side == "a" else 16399, 6),
+                                        (5, 4), (31 if side == "a" else 8191, 1)]):
+        sa = _padded_scales(np.full((M, nb), 127, np.uint8), 8)
+        sb = _padded_scales(np.full((N, nb), 127, np.uint8), 8)
+        (sa if side == "a" else sb)[row, blk] = 130
+        d, _, st = run_mx(ones_a, sa, ones_b, sb, M, N, K, label=f"strip block probe {side} {row},{blk}")
+        assert st == tg.TG_OK
+        want = np.full((M, N), float(K))
+        if side == "a":
+            want[row, :] += 7 * 32
+        else:
+            want[:, row] += 7 * 32
+        assert np.array_equal(d.astype(np.float64), want), f"probe {probe}: row {row} block {blk}"
+
+
+def test_strip_zero_k():
+    """K = 0 on the strip: every element +0 (no K-tile runs)."""
+    M, N = 64, 16400
+    a = np.zeros((M, 16), np.uint8)
+    s = np.zeros((M, 4), np.uint8)
+    b = np.zeros((N, 16), np.uint8)
+    sb = np.zeros((N, 4), np.uint8)
+    assert _plan_name(M, N, 0, 16, 4, 16, 4, N) == STRIP
+    d, full, st = run_mx(a, s, b, sb, M, N, 0, guard=1, label="strip K=0")
+    assert st == tg.TG_OK and np.all(d == 0) and not np.signbit(d).any()
+    assert _guard_ok(full, M, N, 1)
+
+
 def test_zero_k_and_empty():
     a = np.zeros((5, 16), np.uint8)
     s = np.zeros((5, 4), np.uint8)
