@@ -1128,9 +1128,9 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
 // 128×128, 128-byte operand rows in LDS (128 K per stage, two 64-K MFMA
 // K-steps per stage) with the same swizzle and source-side DMA addressing,
 // three A stages and two B stages.  Per iteration t:
-//   K-step 0: the scale words of K-tile t+1 are loaded (eight 4-byte loads
-//             per lane, one per fragment row), then A(t+2) is DMAed;
-//   wait until all but A(t+2) has landed; barrier;
+//   K-step 0: A(t+2) is DMAed;
+//   wait until all but A(t+2) has landed; barrier; (at the first K-tile of
+//   a group) the scale words of the next group are loaded;
 //   K-step 1: B(t+2) is DMAed while the fragments of K-tile t+1's K-step 0
 //             are read.
 // A scale word holds the four blocks of one row in one K-tile; lane r + 32·h
@@ -1299,7 +1299,6 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
         for (int p = 0; p < NPB; ++p)
             g[NPA + p] = MxGroup<MX_GROUP>::load(sb_rsrc, (int)(sb_poff + 2 * p * sb_step + 4 * t0));
     };
-    // words of K-tile j of group g into sw_a[0] / sw_b[0]
     // Words of K-tile t (index j of group g) into sw_a[0] / sw_b[0], ready
     // for the MFMA: blocks at or past K/32 (the tail of a partial last
     // K-tile, and K-tiles past the end) become 2^0 by a wave-uniform byte
