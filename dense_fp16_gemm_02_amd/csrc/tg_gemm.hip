@@ -1480,10 +1480,12 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
 }
 
-// Column-strip variant of the block-scaled GEMM for small M (M <= 64): one
-// 64-row tile row covers all of M, so each workgroup streams its own
-// 128-row band of B exactly once (the fp16 strip tiles' argument: the shape
-// is bound by reading B from HBM, not by the matrix cores).  Four waves
+// 64×128 tiles of the block-scaled GEMM, for small M (M <= 64: one 64-row
+// tile row covers all of M, so each workgroup streams its own 128-row band
+// of B exactly once — the fp16 strip tiles' argument: the shape is bound by
+// reading B from HBM, not by the matrix cores) and for problems with too
+// few 256×256 tiles to occupy the GPU (tiles_m × tiles_n workgroups, column
+// strips innermost).  Four waves
 // split the band by columns (64×32 each: two 32-row A fragments, one B
 // fragment per 64-K step); STAGES LDS stages hold, per 128-K tile, A's 64
 // and B's 128 operand rows (same swizzle and source-side DMA addressing as
@@ -1505,7 +1507,7 @@ template <int STAGES>
 __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ SB, _Float16 *__restrict__ D, int M, int N, int K, int64_t lda,
-    int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd, int dvec)
+    int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd, int tiles_n, int dvec)
 {
     using E = _Float16;
     using V4 = Elem<E>::v4;
@@ -1529,7 +1531,10 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + 4 * SC_SLOT];
     uint8_t *const sc_ring = smem + STAGES * STAGE;  // three slots, then one that empty DMAs fill
 
-    const int n0 = blockIdx.x * BN;
+    // tile (tm, tn) of a tiles_m × tiles_n grid of 64×128 tiles, column
+    // strips innermost
+    const int tm = (int)(blockIdx.x / (unsigned)tiles_n), tn = (int)(blockIdx.x % (unsigned)tiles_n);
+    const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int dr = lane / T::RC, dpc = lane % T::RC;
@@ -1539,7 +1544,7 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
     for (int p = 0; p < A_PASSES; ++p) {
         const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
         a_kc[p] = dpc ^ T::swz(t);
-        a_off[p] = (uint32_t)(imin(t, M - 1) * lda + 16 * a_kc[p]);
+        a_off[p] = (uint32_t)(imin(t, M - 1 - m0) * lda + 16 * a_kc[p]);
     }
 #pragma unroll
     for (int p = 0; p < B_PASSES; ++p) {
@@ -1547,12 +1552,14 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
         b_kc[p] = dpc ^ T::swz(t);
         b_off[p] = (uint32_t)(imin(t, N - 1 - n0) * ldb + 16 * b_kc[p]);
     }
+    const uint8_t *a_band = A + (int64_t)m0 * lda;
     const uint8_t *b_band = B + (int64_t)n0 * ldb;
-    // scale rows from row 0 of A and row n0 of B; rows past M (N) read zero
+    // scale rows from row m0 of A and row n0 of B; rows past M (N) read zero
     // words (they feed only unstored outputs)
     const __amdgpu_buffer_rsrc_t sc_rsrc =
-        wave == 0 ? __builtin_amdgcn_make_buffer_rsrc((void *)SA, (short)0,
-                                                      (int)imin64((int64_t)M * ldsa, DMA_RANGE), BUFFER_RSRC_WORD3)
+        wave == 0 ? __builtin_amdgcn_make_buffer_rsrc((void *)(SA + (int64_t)m0 * ldsa), (short)0,
+                                                      (int)imin64((int64_t)(M - m0) * ldsa, DMA_RANGE),
+                                                      BUFFER_RSRC_WORD3)
                   : __builtin_amdgcn_make_buffer_rsrc((void *)(SB + (int64_t)n0 * ldsb), (short)0,
                                                       (int)imin64((int64_t)(N - n0) * ldsb, DMA_RANGE),
                                                       BUFFER_RSRC_WORD3);
@@ -1580,7 +1587,7 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
         uint8_t *st = smem + (t % STAGES) * STAGE;
         const int klim = live ? K - kt * BKB : 0;  // valid bytes of each row in this K-tile
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(A + (int64_t)kt * BKB), (short)0, live ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
+            (void *)(a_band + (int64_t)kt * BKB), (short)0, live ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(b_band + (int64_t)kt * BKB), (short)0, live ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
 #pragma unroll
@@ -1699,7 +1706,7 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
                 const int c = j * 32 + g * 8 + frag_hi * 4;
                 *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
             }
-    store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, 0, n0 + wave * WTN, M, N, dvec, lane);
+    store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0, n0 + wave * WTN, M, N, dvec, lane);
 }
 
 struct KernelChoice {
@@ -1975,14 +1982,19 @@ extern "C" int tg_gemm_bf16_plan(const void *A, const void *B, const void *D, in
 }
 
 // Block-scaled FP8 entry point: argument checks, then one 256×256 tile per
-// workgroup, or for M <= 64 and N of at least 128 column strips one 64×128
-// strip per workgroup.
+// workgroup, or one 64×128 tile per workgroup where M <= 64 and N gives at
+// least 128 column strips (HBM-bound: B streams once) or where the problem
+// has too few 256×256 tiles to occupy a quarter of the GPU.
 constexpr const char *MXF8_KERNEL = "gemm_mxf8_256x256_w2x2_dma";
 constexpr const char *MXF8_STRIP_KERNEL = "gemm_mxf8_64x128_w1x4_dma";
 #ifndef TG_MX_STRIP_STAGES
 #define TG_MX_STRIP_STAGES 4
 #endif
-bool mx_uses_strip(int64_t M, int64_t N) { return M <= 64 && (N + 127) / 128 >= NUM_CU / 2; }
+bool mx_uses_strip(int64_t M, int64_t N)
+{
+    return (M <= 64 && (N + 127) / 128 >= NUM_CU / 2) || ((M + 255) / 256) * ((N + 255) / 256) < NUM_CU / 4;
+}
+int64_t mx_strip_tiles(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 127) / 128); }
 
 int validate_mx(const void *A, const void *SA, const void *B, const void *SB, const void *D, int64_t M,
                 int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd)
@@ -2017,11 +2029,14 @@ extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const 
     int Mi = (int)M, Ni = (int)N, Ki = (int)K;
     int dvec = (ldd % 8 == 0) && ((uintptr_t)D % 16 == 0);
     if (mx_uses_strip(M, N)) {
+        const int64_t sgrid = mx_strip_tiles(M, N);
+        if (sgrid >= LIMIT32)
+            return TG_ERR_TOO_LARGE;
+        int stiles_n = (int)((N + 127) / 128);
         void *sargs[] = {(void *)&A, (void *)&SA, (void *)&B, (void *)&SB, (void *)&D, &Mi, &Ni, &Ki,
-                         &lda, &ldsa, &ldb, &ldsb, &ldd, &dvec};
+                         &lda, &ldsa, &ldb, &ldsb, &ldd, &stiles_n, &dvec};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemm_mxf8_strip_kernel<TG_MX_STRIP_STAGES>),
-                                       dim3((unsigned)((N + 127) / 128)), dim3(256), sargs, 0,
-                                       (hipStream_t)stream);
+                                       dim3((unsigned)sgrid), dim3(256), sargs, 0, (hipStream_t)stream);
         return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
     }
     int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
@@ -2055,7 +2070,7 @@ extern "C" int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, c
     if (name && name_len > 0)
         snprintf(name, (size_t)name_len, "%s", strip ? MXF8_STRIP_KERNEL : MXF8_KERNEL);
     if (tiles)
-        *tiles = strip ? (N + 127) / 128 : ((M + 255) / 256) * ((N + 255) / 256);
+        *tiles = strip ? mx_strip_tiles(M, N) : ((M + 255) / 256) * ((N + 255) / 256);
     return TG_OK;
 }
 

@@ -142,9 +142,10 @@ def test_mxf8_plans_and_validation():
         if w.K % 32:
             assert st == tg.TG_ERR_LAYOUT and name == "" and tiles == 0
             continue
-        if w.M <= 64 and (w.N + 127) // 128 >= 128:  # column strips for small M
+        big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)
+        if (w.M <= 64 and (w.N + 127) // 128 >= 128) or big_tiles < 64:  # 64x128 tiles
             assert st == tg.TG_OK and name == "gemm_mxf8_64x128_w1x4_dma"
-            assert tiles == (w.N + 127) // 128
+            assert tiles == ((w.M + 63) // 64) * ((w.N + 127) // 128)
         else:
             assert st == tg.TG_OK and name == "gemm_mxf8_256x256_w2x2_dma"
             assert tiles == ((w.M + 255) // 256) * ((w.N + 255) // 256)
@@ -154,6 +155,11 @@ def test_mxf8_plans_and_validation():
     assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 16384, 128, 128, 4, 128, 4, 16384)[1] == \
         "gemm_mxf8_256x256_w2x2_dma"
     assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 16256, 128, 128, 4, 128, 4, 16256)[1] == \
+        "gemm_mxf8_256x256_w2x2_dma"
+    # and problems with fewer than 64 tiles of 256x256 take 64x128 tiles
+    assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 1792, 128, 128, 4, 128, 4, 1792)[1:] == \
+        ("gemm_mxf8_64x128_w1x4_dma", 32 * 14)
+    assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 2048, 128, 128, 4, 128, 4, 2048)[1] == \
         "gemm_mxf8_256x256_w2x2_dma"
     ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 128, 128, 4, 128, 4, 64)
     assert tg.tg_gemm_mxf8_plan(*ok)[0] == tg.TG_OK

@@ -74,6 +74,17 @@ def _ld4(n):
     return max(4, (n + 3) // 4 * 4)
 
 
+STRIP = "gemm_mxf8_64x128_w1x4_dma"
+BIG = "gemm_mxf8_256x256_w2x2_dma"
+
+
+def _plan_name(M, N, K, lda, ldsa, ldb, ldsb, ldd):
+    st, name, tiles = tg.tg_gemm_mxf8_plan(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+                                           M, N, K, lda, ldsa, ldb, ldsb, ldd)
+    assert st == tg.TG_OK
+    return name
+
+
 SMALL = [w for w in workloads.WORKLOADS if w.M * w.N * w.K <= 2 ** 31]
 
 
@@ -105,13 +116,16 @@ def _pm1(seed, rows, K):
     return rng.choice(np.array([ONE, MINUS_ONE, ZERO], np.uint8), size=(rows, K))
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 520, 256), (77, 600, 1024), (513, 129, 96)])
-def test_unit_scales_exact(M, N, K):
+@pytest.mark.parametrize("M,N,K,kernel", [(256, 256, 128, STRIP), (300, 520, 256, STRIP), (77, 600, 1024, STRIP),
+                                          (513, 129, 96, STRIP), (2100, 2050, 128, BIG), (2049, 2100, 96, BIG)])
+def test_unit_scales_exact(M, N, K, kernel):
     """Values in {-1, 0, 1} with unit scales: D is an integer ≤ K, exact in
-    fp32 and fp16, so every element must match the oracle bit for bit."""
+    fp32 and fp16, so every element must match the oracle bit for bit (on
+    both kernels: 64×128 tiles for small problems, 256×256 for large)."""
     a, b = _pm1(11 + K, M, K), _pm1(12 + K, N, K)
     sa = np.full((M, _ld4(K // 32)), 127, np.uint8)
     sb = np.full((N, _ld4(K // 32)), 127, np.uint8)
+    assert _plan_name(M, N, K, K, sa.shape[1], K, sb.shape[1], N + 4) == kernel
     res = oracle.gemm_mx(a, sa, b, sb, M, N, K)
     d, full, st = run_mx(a, sa, b, sb, M, N, K, guard=2, label="unit scales")
     assert st == tg.TG_OK
@@ -119,8 +133,9 @@ def test_unit_scales_exact(M, N, K):
     assert _guard_ok(full, M, N, 2)
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (190, 333, 384), (260, 260, 96)])
-def test_random_scales_exact(M, N, K):
+@pytest.mark.parametrize("M,N,K,kernel", [(256, 256, 256, STRIP), (190, 333, 384, STRIP), (260, 260, 96, STRIP),
+                                          (2100, 2060, 256, BIG), (2070, 2090, 96, BIG)])
+def test_random_scales_exact(M, N, K, kernel):
     """Values ±1 and 0 with scales 2^-3..2^3 per block: every partial sum is a
     multiple of 2^-6 below 2^12, exact in fp32, so D is bit-exact.  A scale
     applied to the wrong block, lane half or operand changes D."""
@@ -129,6 +144,7 @@ def test_random_scales_exact(M, N, K):
     nb = K // 32
     sa = _padded_scales(rng.integers(124, 131, size=(M, nb)).astype(np.uint8), _ld4(nb))
     sb = _padded_scales(rng.integers(124, 131, size=(N, nb)).astype(np.uint8), _ld4(nb))
+    assert _plan_name(M, N, K, K, sa.shape[1], K, sb.shape[1], N) == kernel
     res = oracle.gemm_mx(a, sa, b, sb, M, N, K)
     d, _, st = run_mx(a, sa, b, sb, M, N, K, label="random scales")
     assert st == tg.TG_OK
@@ -136,14 +152,16 @@ def test_random_scales_exact(M, N, K):
 
 
 @pytest.mark.parametrize("side", ["a", "b"])
-def test_each_block_scale_lands_on_its_block(side):
+@pytest.mark.parametrize("M,N", [(260, 270), (2100, 2060)])
+def test_each_block_scale_lands_on_its_block(side, M, N):
     """All-ones operands with unit scales except one block of one row per
-    probe: that row (column) of D gains exactly 7·32, nothing else moves."""
-    M, N, K = 260, 270, 224   # two K-tiles, the second partial (blocks 4..6)
+    probe: that row (column) of D gains exactly 7·32, nothing else moves
+    (64×128 tiles at 260×270, 256×256 tiles at 2100×2060)."""
+    K = 224   # two K-tiles, the second partial (blocks 4..6)
     nb = K // 32
     ones_a = np.full((M, K), ONE, np.uint8)
     ones_b = np.full((N, K), ONE, np.uint8)
-    for probe, (row, blk) in enumerate([(0, 0), (1, 1), (33, 2), (31, 3), (64, 4), (259 if side == "a" else 269, 6)]):
+    for probe, (row, blk) in enumerate([(0, 0), (1, 1), (33, 2), (31, 3), (64, 4), ((M if side == "a" else N) - 1, 6)]):
         sa = _padded_scales(np.full((M, nb), 127, np.uint8), 8)
         sb = _padded_scales(np.full((N, nb), 127, np.uint8), 8)
         (sa if side == "a" else sb)[row, blk] = 130
@@ -157,12 +175,12 @@ def test_each_block_scale_lands_on_its_block(side):
         assert np.array_equal(d.astype(np.float64), want), f"probe {probe}: row {row} block {blk}"
 
 
-@pytest.mark.parametrize("K", [32, 96, 160, 4096 + 96])
-def test_partial_k_tiles_and_nan_padding(K):
+@pytest.mark.parametrize("M,N,K", [(300, 280, 32), (300, 280, 96), (300, 280, 160), (300, 280, 4096 + 96),
+                                   (2090, 2080, 32), (2090, 2080, 160), (2090, 2080, 1024 + 96)])
+def test_partial_k_tiles_and_nan_padding(M, N, K):
     """K not a multiple of the 128-element stage: the missing elements are
     read as zero and their scale bytes (NaN here) are never applied; operand
-    padding past K holds the NaN code."""
-    M, N = 300, 280
+    padding past K holds the NaN code (both kernels)."""
     # scales 2^-15..2^-9 keep |D| far below fp16's range for any codes
     qa, sa = workloads.random_mx(31 + K, M, K, 112, 118)
     qb, sb = workloads.random_mx(32 + K, N, K, 112, 118)
@@ -176,16 +194,6 @@ def test_partial_k_tiles_and_nan_padding(K):
     assert st == tg.TG_OK
     _check(d, res, f"K={K}")
     assert _guard_ok(full, M, N, 2)
-
-
-STRIP = "gemm_mxf8_64x128_w1x4_dma"
-
-
-def _plan_name(M, N, K, lda, ldsa, ldb, ldsb, ldd):
-    st, name, tiles = tg.tg_gemm_mxf8_plan(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
-                                           M, N, K, lda, ldsa, ldb, ldsb, ldd)
-    assert st == tg.TG_OK
-    return name
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 16400, 1024), (37, 16411, 224), (1, 16385, 32), (64, 16384, 4096 + 96)])
