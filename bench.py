@@ -462,6 +462,14 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    import dense_fp16_gemm_02_amd as tg
+    st, cus, clk_khz, arch = tg.tg_device_info()
+    if st == tg.TG_OK:
+        # dense matrix-core flop per clock per CU: 4096 for fp16/bf16 (2.5 PFLOP/s
+        # = 256 CUs × 4096 × 2.4 GHz), twice that for fp8
+        per_clk = 8192 if args.dtype == "mxf8" else 4096
+        line["device"] = {"arch": arch, "compute_units": cus, "max_sclk_mhz": clk_khz / 1000,
+                          "derived_peak_tflops": round(cus * per_clk * clk_khz * 1e3 / 1e12, 1)}
     if len(r["records_ms"]) > 1:
         line["records_ms_per_step"] = [round(x, 6) for x in r["records_ms"]]
     if r["per_call_us"]:

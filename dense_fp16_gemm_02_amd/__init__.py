@@ -8,6 +8,7 @@ not built, importing the functions below raises.
     tg_gemm_f16_plan(A, B, D, M, N, K, lda, ldb, ldd) -> (status, name, tiles)
     tg_gemm_bf16(...), tg_gemm_bf16_plan(...)   the same for bfloat16 data
     tg_status_string(status) -> str
+    tg_device_info() -> (status, compute_units, max_clock_khz, arch)
     gemm(A, B, out=None, stream=None) -> D   (torch wrapper; fp16 or bf16)
 
 Pointers may be given as torch tensors (their ``data_ptr()``) or integers;
@@ -22,7 +23,7 @@ import os
 __all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_ERR_TOO_LARGE",
            "TG_ERR_LAYOUT", "tg_gemm_mxf8", "tg_gemm_mxf8_plan",
            "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_gemm_bf16",
-           "tg_gemm_bf16_plan", "tg_status_string", "gemm"]
+           "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "gemm"]
 
 TG_OK = 0
 TG_ERR_INVALID_ARG = -1
@@ -71,6 +72,9 @@ def load():
     lib.tg_gemm_mxf8_plan.argtypes = [vp] * 5 + [i64] * 8 + [ctypes.c_char_p, i64, ctypes.POINTER(i64)]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_status_string.argtypes = [ctypes.c_int]
+    lib.tg_device_info.restype = ctypes.c_int
+    lib.tg_device_info.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                   ctypes.c_char_p, i64]
     _lib = lib
     return lib
 
@@ -140,6 +144,14 @@ def tg_gemm_mxf8_plan(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldsa: i
 
 def tg_status_string(status: int) -> str:
     return load().tg_status_string(status).decode()
+
+
+def tg_device_info():
+    """(status, compute_units, max_clock_khz, arch) of the current device."""
+    cus, clk = ctypes.c_int(0), ctypes.c_int(0)
+    arch = ctypes.create_string_buffer(64)
+    st = load().tg_device_info(ctypes.byref(cus), ctypes.byref(clk), arch, len(arch))
+    return st, cus.value, clk.value, arch.value.decode()
 
 
 def gemm(A, B, out=None, stream=None):

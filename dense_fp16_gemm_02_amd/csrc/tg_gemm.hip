@@ -2074,6 +2074,25 @@ extern "C" int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, c
     return TG_OK;
 }
 
+extern "C" int tg_device_info(int *compute_units, int *max_clock_khz, char *arch, int64_t arch_len)
+{
+    int dev = 0, cus = 0, clk = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return TG_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&clk, hipDeviceAttributeClockRate, dev) != hipSuccess ||
+        hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return TG_ERR_DEVICE;
+    if (compute_units)
+        *compute_units = cus;
+    if (max_clock_khz)
+        *max_clock_khz = clk;
+    if (arch && arch_len > 0)
+        snprintf(arch, (size_t)arch_len, "%s", prop.gcnArchName);
+    return TG_OK;
+}
+
 extern "C" const char *tg_status_string(int status)
 {
     switch (status) {

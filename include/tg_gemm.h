@@ -163,6 +163,16 @@ int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, const void *
 /* tg_status_string — a static, NUL-terminated description of a status. */
 const char *tg_status_string(int status);
 
+/* tg_device_info — the current device's compute-unit count, its maximum
+ * shader clock in kHz and its architecture name (NUL-terminated, truncated
+ * to arch_len bytes; arch may be NULL).  Lets a caller derive the dense
+ * matrix-core peak as CUs × flop per clock per CU × clock, the figure the
+ * peak percentages of the measurements rest on.  Outputs are written only on
+ * success; NULL output pointers are skipped.  Host-only, synchronous, no
+ * kernel launch.  Returns TG_OK, or TG_ERR_DEVICE if no device is
+ * available or a runtime query fails. */
+int tg_device_info(int *compute_units, int *max_clock_khz, char *arch, int64_t arch_len);
+
 #ifdef __cplusplus
 }
 #endif

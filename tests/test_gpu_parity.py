@@ -280,6 +280,15 @@ def test_large_tile_short_k_exact(K):
     assert np.array_equal(d[rows].astype(np.int64), want)
 
 
+def test_device_info():
+    """tg_device_info reports the device the peak figures assume: gfx950, 256
+    compute units, a maximum shader clock near 2.4 GHz."""
+    st, cus, clk_khz, arch = tg.tg_device_info()
+    say(f"device info: {arch} {cus} CUs {clk_khz} kHz")
+    assert st == tg.TG_OK and arch.startswith("gfx950")
+    assert cus == 256 and 2_000_000 <= clk_khz <= 3_000_000
+
+
 # ------------------------------------------------------- degenerate cases
 
 def test_zero_k_gives_positive_zero():
