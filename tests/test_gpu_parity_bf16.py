@@ -68,6 +68,7 @@ def test_workload_sampled_rows(idx):
 @pytest.mark.parametrize("M,N,K,tile", [
     (128, 128, 64, "64x64"), (1000, 1000, 200, "64x64"), (257, 263, 136, "64x64"),
     (2100, 2000, 256, "128x128"), (4352 - 5, 4352 - 3, 136, "256x256"),
+    (4136, 4120, 8, "256x256"), (4136, 4120, 72, "256x256"),
     (64, 16411, 200, "64x128"), (100, 16390, 256, "128x128"), (200, 16500, 136, "256x128"),
 ])
 def test_small_int_pattern_exact(M, N, K, tile):
