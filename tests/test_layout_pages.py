@@ -159,6 +159,22 @@ def test_mfma_fragment_specs_parse_as_documented():
             assert r == 8 * (v // 4) + 4 * (l // 32) + v % 4 and c == l % 32
             seen.add((l, v))
     assert len(seen) == 1024
+    # the 16×16×32 shape of the 256×256 kernel: operand lane = row + 16·(k/8),
+    # element k mod 8; accumulator (inputs swapped) D row = lane mod 16,
+    # D col = 4·(lane/16) + register
+    op16 = "S[(16,4,8):(1@laneid,16@laneid,1@m)]"
+    for row in range(16):
+        for k in range(32):
+            assert lay.apply(op16, row, k, shape=[16, 32]) == {"laneid": row + 16 * (k // 8), "m": k % 8}
+    acc16 = "S[(16,4,4):(1@laneid,16@laneid,1@m)]"
+    seen = set()
+    for r in range(16):
+        for c in range(16):
+            got = lay.apply(acc16, r, c, shape=[16, 16])
+            v, l = got["m"], got["laneid"]
+            assert r == l % 16 and c == 4 * (l // 16) + v
+            seen.add((l, v))
+    assert len(seen) == 256
 
 
 def _fragment_read_addrs(compose, rows_base=0, kk=0):
