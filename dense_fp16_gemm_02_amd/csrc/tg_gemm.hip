@@ -1733,7 +1733,7 @@ struct KernelChoice {
 #define TG_M_STAGES 2
 #endif
 #ifndef TG_S_BK
-#define TG_S_BK 32
+#define TG_S_BK 64
 #endif
 #ifndef TG_S_STAGES
 #define TG_S_STAGES 4
