@@ -1721,7 +1721,7 @@ struct KernelChoice {
 // S: 64×64, K*: column strips; the 256×256 tile uses gemm_dma3_kernel).
 // The defaults are the measured best on MI355X.
 #ifndef TG_M_DMA_STEPS
-#define TG_M_DMA_STEPS 1
+#define TG_M_DMA_STEPS 2
 #endif
 #ifndef TG_S_DMA_STEPS
 #define TG_S_DMA_STEPS 2
@@ -1730,7 +1730,7 @@ struct KernelChoice {
 #define TG_M_BK 64
 #endif
 #ifndef TG_M_STAGES
-#define TG_M_STAGES 2
+#define TG_M_STAGES 4
 #endif
 #ifndef TG_S_BK
 #define TG_S_BK 64
