@@ -529,7 +529,17 @@ __device__ inline void store_staged_block(const E *stg, SO stage_off, E *__restr
 //   0 is read and the drained stage is refilled with K-tile kt+STAGES (past
 //   the end: an all-out-of-range DMA, i.e. a no-op that keeps the loop
 //   branch-free and the vmcnt bookkeeping uniform).
-template <typename E, int BM, int BN, int WM, int WN, int BK_, int STAGES, int OCC, int DMA_STEPS, int KROT>
+template <int MF>
+struct AccOf {
+    typedef f32x16 type;  // 32×32 MFMA: 16 fp32 per lane
+};
+template <>
+struct AccOf<16> {
+    typedef f32x4 type;  // 16×16 MFMA: 4 fp32 per lane
+};
+
+template <typename E, int BM, int BN, int WM, int WN, int BK_, int STAGES, int OCC, int DMA_STEPS, int KROT,
+          int MF = 32>
 __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? WM * WN / 4 : 1)) void gemm_dma_kernel(
     const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
@@ -540,12 +550,17 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
     using T = OperandTile<BK_>;
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int KSTEPS = BK_ / 16;
+    using Acc = typename AccOf<MF>::type;
+    constexpr int TM = WTM / MF, TN = WTN / MF;
+    constexpr int KW = MF == 32 ? 16 : 32;  // K per MFMA
+    constexpr int KSTEPS = BK_ / KW;
+    constexpr int CPK = KW / 8;  // 16-byte chunks per row per K-step
+    constexpr int ACC_REGS = MF * MF / 64;
     constexpr int A_PASSES = BM / T::ROWS_PER_DMA / NW, B_PASSES = BN / T::ROWS_PER_DMA / NW;
     constexpr int DMA_PER_TILE = A_PASSES + B_PASSES;
     constexpr int STAGE = (BM + BN) * BK_;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(MF == 32 || MF == 16, "32×32×16 or 16×16×32 MFMA");
+    static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
     static_assert((BM / T::ROWS_PER_DMA) % NW == 0 && (BN / T::ROWS_PER_DMA) % NW == 0,
                   "DMA row groups must split evenly over the waves");
     static_assert(KSTEPS % 2 == 0, "fragment buffers alternate per K-step");
@@ -626,28 +641,29 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
                   8 * b_kc[i - A_PASSES] < d.klim ? b_off[i - A_PASSES] : DMA_OOB);
     };
 
-    const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
+    const int frag_row = MF == 32 ? frag_row_of(lane) : frag16_row_of(lane);
+    const int frag_hi = MF == 32 ? frag_hi_of(lane) : frag16_hi_of(lane);
     V8 fa[2][TM], fb[2][TN];
     // one fragment of K-step kk of the K-tile in stage s: q < TM is A
     // fragment q, else B fragment q - TM
     auto read_frag = [&](int s, int kk, int q, V8 *a, V8 *b) {
         const E *as = smem + s * STAGE;
         const E *bs = as + BM * BK_;
-        const int c = kk * 2 + frag_hi;
+        const int c = kk * CPK + frag_hi;
         if (q < TM)
-            a[q] = *reinterpret_cast<const V8 *>(as + T::off(wm * WTM + q * 32 + frag_row, c));
+            a[q] = *reinterpret_cast<const V8 *>(as + T::off(wm * WTM + q * MF + frag_row, c));
         else
             b[q - TM] = *reinterpret_cast<const V8 *>(
-                bs + T::off(wn * WTN + (q - TM) * 32 + frag_row, c));
+                bs + T::off(wn * WTN + (q - TM) * MF + frag_row, c));
     };
 
-    f32x16 acc[TM][TN];
+    Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
+            for (int v = 0; v < ACC_REGS; ++v)
                 acc[i][j][v] = 0.0f;
 
     // One K-step's TM·TN MFMAs on fragments (a, b), with the companion work
@@ -747,8 +763,12 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
         const DmaTile d = dma_tile(kt + STAGES);
         step(fa[1], fb[1], true, (kt + 1) % STAGES, 0, fa[0], fb[0], &d, 0, P1, EVERY_POST);
     }
-    if (KT > 0) {
-        leading_steps((KT - 1) % STAGES, KT - 1 + STAGES - 1);
+    // the last K-tile (with 16×16 MFMAs without a branch: a conditional tail
+    // makes the register allocator rotate accumulators; with K = 0 it reads
+    // stage 0, which the prologue filled with zeros — every DMA there read
+    // past the range — so it adds nothing)
+    if (MF == 16 || KT > 0) {
+        leading_steps(KT > 0 ? (KT - 1) % STAGES : 0, KT - 1 + STAGES - 1);
         step(fa[1], fb[1], false, 0, 0, fa[0], fb[0], nullptr, 0, 0, 1);
     }
     wait_vmem<0>();  // no LDS DMA may be outstanding when the wave ends
@@ -774,13 +794,14 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g = 0; g < ACC_REGS / 4; ++g) {
                 V4 h;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     h[r] = (E)acc[i][j][g * 4 + r];  // round to nearest even
-                const int r = i * 32 + frag_row;
-                const int c = j * 32 + g * 8 + frag_hi * 4;
+                // four consecutive D columns of row r
+                const int r = i * MF + frag_row;
+                const int c = j * MF + (MF == 32 ? g * 8 + frag_hi * 4 : frag_hi * 4);
                 *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
             }
     store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
@@ -806,15 +827,6 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
 // one DMA every eighth MFMA.  Everything else (swizzle, fragment reads, staged epilogue) is as in
 // gemm_dma_kernel; rows past M or N are clamped, and a K that is not a
 // multiple of 64 makes the first K-tile (not the last) the partial one.
-template <int MF>
-struct AccOf {
-    typedef f32x16 type;  // 32×32 MFMA: 16 fp32 per lane
-};
-template <>
-struct AccOf<16> {
-    typedef f32x4 type;  // 16×16 MFMA: 4 fp32 per lane
-};
-
 template <typename E, int BM, int BN, int WM, int WN, int MF>
 __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_kernel(
     const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
@@ -1744,6 +1756,15 @@ struct KernelChoice {
 #ifndef TG_M_KROT
 #define TG_M_KROT 0
 #endif
+// MFMA shape per tile (16: v_mfma_f32_16x16x32, 32: v_mfma_f32_32x32x16).
+// The 64×64 tile runs faster with the 16×16 shape (10–15% on 1000³, 1024³,
+// 512×512×4096); the 128×128 tile measured mixed (−5% to +2%), so keeps 32.
+#ifndef TG_M_MF
+#define TG_M_MF 32
+#endif
+#ifndef TG_S_MF
+#define TG_S_MF 16
+#endif
 
 // MFMA shape of the 256×256 kernel: 16 (v_mfma_f32_16x16x32, the default:
 // the same work in twice the instructions draws less power, so the clock
@@ -1757,13 +1778,13 @@ struct KernelChoice {
 enum LoadPath { PATH_DMA = 0, PATH_VEC = 1, PATH_SCALAR = 2 };
 
 template <typename E, int BM, int BN, int WM, int WN, int DMA_BK, int DMA_STAGES,
-          int DMA_STEPS = 1, int OCC = 1, int KROT = 0>
+          int DMA_STEPS = 1, int OCC = 1, int KROT = 0, int MF = 32>
 KernelChoice choice(LoadPath path, const char *tile)
 {
     const void *fn =
         path == PATH_DMA
             ? reinterpret_cast<const void *>(
-                  &gemm_dma_kernel<E, BM, BN, WM, WN, DMA_BK, DMA_STAGES, OCC, DMA_STEPS, KROT>)
+                  &gemm_dma_kernel<E, BM, BN, WM, WN, DMA_BK, DMA_STAGES, OCC, DMA_STEPS, KROT, MF>)
         : path == PATH_VEC ? reinterpret_cast<const void *>(&gemm_vec_kernel<E, BM, BN, WM, WN, true>)
                            : reinterpret_cast<const void *>(&gemm_vec_kernel<E, BM, BN, WM, WN, false>);
     return {fn, tile, BM, BN, WM * WN * 64, path};
@@ -1873,11 +1894,11 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
             k = choice<E, 256, 256, 2, 2, 64, 2>(lp, TILE_256);
     }
     else if (tiles(128, 128) >= NUM_CU)
-        k = choice<E, 128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT>(path(128, 128),
-                                                                                       TILE_128);
+        k = choice<E, 128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT, TG_M_MF>(
+            path(128, 128), TILE_128);
     else
-        k = choice<E, 64, 64, 2, 2, TG_S_BK, TG_S_STAGES, TG_S_DMA_STEPS, 1, TG_S_KROT>(path(64, 64),
-                                                                                     TILE_64);
+        k = choice<E, 64, 64, 2, 2, TG_S_BK, TG_S_STAGES, TG_S_DMA_STEPS, 1, TG_S_KROT, TG_S_MF>(
+            path(64, 64), TILE_64);
     Plan p;
     p.k = k;
     p.tiles_m = (int)((M + k.bm - 1) / k.bm);
