@@ -1885,7 +1885,11 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     else if (TG_K_ON && M <= 256 && TG_K_MAXM >= 256 && tiles(256, 128) >= NUM_CU / 2)
         k = choice<E, 256, 128, 2, 2, TG_K4_BK, TG_K4_STAGES, 2, 1, 1>(path(256, 128), TILE_STRIP256);
     else
-    if (tiles(256, 256) >= NUM_CU) {
+    // the 256×256 kernel from 160 tiles on (5/8 of the CUs busy): it beats
+    // the 128×128 tiles by 20–40% at 160–224 tiles (the 128×128 grid then
+    // runs 2.5–3.5 waves); at 128 tiles (exactly two waves of 128×128) the
+    // smaller tile is 5–9% faster
+    if (tiles(256, 256) >= 5 * NUM_CU / 8) {
         const LoadPath lp = path(256, 256);
         if (lp == PATH_DMA)
             k = {reinterpret_cast<const void *>(&gemm_dma3_kernel<E, 256, 256, 2, 2, TG_L_MF>), TILE_256, 256,

@@ -264,6 +264,22 @@ def test_second_wave_zero_k():
     assert np.all(_bits(d) == 0)
 
 
+def test_fewer_large_tiles_than_cus():
+    """One GPU's share of the linear layer split by columns over eight GPUs,
+    8192×1792×4096: 224 tiles of 256×256 on 256 CUs, which the largest tile
+    takes from 160 tiles on; 66 sampled rows against the oracle."""
+    M, N, K = 8192, 1792, 4096
+    a = workloads.random_f16(93, (M, K))
+    b = workloads.random_f16(94, (N, K), ("normal", 0.0, 1.0 / 64))
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N)
+    say(f"column-split plan {name} tiles={tiles}")
+    assert name.startswith("gemm_f16_256x256_") and tiles == 224
+    d, full, st = run(a, b, M, N, K, guard=1, label="column split")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 1)
+    rows = workloads.sample_rows(workloads.Workload(8, "split", M, N, K, (), ()), 64)
+    _check(d[rows], oracle.gemm(a, b, M, N, K, rows=rows), "column split")
+
+
 @pytest.mark.parametrize("K", [8, 64, 72, 120])
 def test_large_tile_short_k_exact(K):
     """Short K through the 256×256 kernel: one K-tile (K = 8, 64) or two whose
