@@ -1897,7 +1897,11 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
         else
             k = choice<E, 256, 256, 2, 2, 64, 2>(lp, TILE_256);
     }
-    else if (tiles(128, 128) >= NUM_CU)
+    // 128×128 tiles from 80 of them on: at 81–224 tiles they beat the 64×64
+    // grid by 15–90% (1152²×1024, 1024×1536×4096, 2048×1280×4096,
+    // 1792×2048×2048); at 48–64 (1000³, 1024²×4096, 768×1024×4096) the
+    // 64×64 grid is faster
+    else if (tiles(128, 128) >= 5 * NUM_CU / 16)
         k = choice<E, 128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT, TG_M_MF>(
             path(128, 128), TILE_128);
     else
