@@ -147,6 +147,27 @@ def traffic_record(args) -> int:
     return 0
 
 
+def trace_summary(csv_path: str, name_part: str, window=None) -> dict:
+    """Per-dispatch durations of the kernels whose name contains `name_part`
+    in a rocprofv3 --kernel-trace kernel_trace.csv, in dispatch order, with
+    their mean over the call window [lo, hi) when given (the timed calls of a
+    bench run: calls warmup .. warmup+steps-1)."""
+    import csv
+
+    rows = [r for r in csv.DictReader(open(csv_path)) if name_part in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    out = {"kernel": rows[0]["Kernel_Name"] if rows else None, "calls": len(us), "per_call_us": us}
+    if us:
+        out["mean_us"] = sum(us) / len(us)
+    if window and us:
+        lo, hi = window
+        sel = us[lo:hi]
+        out["window"] = [lo, hi]
+        out["window_mean_us"] = sum(sel) / len(sel) if sel else None
+    return out
+
+
 def copy_only(nbytes: int, reps: int = 5) -> int:
     """A plain device-to-device copy of `nbytes` (the calibration kernel)."""
     import torch
@@ -329,6 +350,54 @@ def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16"):
     }
 
 
+def mfma_ceiling(w, args) -> int:
+    """Time tg_mfma_ceiling (a stream of independent MFMAs on register
+    operands, no memory traffic) with the same protocol as the GEMM: the
+    operand registers loaded from the workload's own A and B (its value
+    distribution), and from zeros (no toggling, so no power limit).  Prints
+    one JSON line with TFLOP/s per MFMA shape and operand set."""
+    import numpy as np
+    import torch
+
+    import dense_fp16_gemm_02_amd as tg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    a, b = workloads.make_inputs(w)
+    A = torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16).reshape(-1)
+    B = torch.from_numpy(b.view(np.int16)).to(dev).view(torch.float16).reshape(-1)
+    Z = torch.zeros(1 << 16, dtype=torch.float16, device=dev)
+    st, cus, clk_khz, arch = tg.tg_device_info()
+    if st != tg.TG_OK:
+        raise RuntimeError(tg.tg_status_string(st))
+    out = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    iters = args.ceiling_iters
+    flop = cus * 4 * iters * float(1 << 20)
+    results = {}
+    for shape in (16, 32):
+        for label, (x, y) in (("workload", (A, B)), ("zeros", (Z, Z))):
+            def step(i, x=x, y=y, shape=shape):
+                s = tg.tg_mfma_ceiling(shape, x, x.numel(), y, y.numel(), 1, iters, cus, out, stream)
+                if s != tg.TG_OK:
+                    raise RuntimeError(f"tg_mfma_ceiling: {tg.tg_status_string(s)}")
+
+            t = _timed(step, args.steps, args.warmup, max(1, args.records), args.per_call, dev, stream)
+            tf = flop / (t["ms"] * 1e-3) / 1e12
+            name = f"mfma_{shape}x{shape}x{512 // shape}_f16_{label}"
+            results[name] = {"ms_per_launch": round(t["ms"], 6), "tflops": round(tf, 1),
+                             "frac_of_peak": round(tf / PEAK_FP16_TFLOPS, 4)}
+            log(f"{name:36s} {t['ms'] * 1e3:9.2f} us/launch {tf:8.1f} TFLOP/s "
+                f"({100 * tf / PEAK_FP16_TFLOPS:.1f}% of {PEAK_FP16_TFLOPS:.0f})")
+    line = {"metric": "TFLOP/s of a matrix-core stream with no memory traffic (tg_mfma_ceiling)",
+            "unit": "TFLOP/s", "workload_operands": w.name, "workgroups": cus, "iters": iters,
+            "steps": args.steps, "warmup": args.warmup, "peak": PEAK_FP16_TFLOPS,
+            "device": {"arch": arch, "compute_units": cus, "max_sclk_mhz": clk_khz / 1000},
+            "results": results}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def algorithmic_bytes(w, dtype: str) -> int:
     """Compulsory HBM bytes of one call: A and B read once, D (fp16) written once;
     the block-scaled entry point reads 1-byte codes plus one scale byte per 32 K
@@ -352,6 +421,13 @@ def main() -> int:
                     help="target length of the oracle sample")
     ap.add_argument("--cpu-rows", type=int, default=None, help="fixed oracle sample size in rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-cpu-seconds", type=float, default=6.0,
+                    help="with --all: length of each workload's oracle sample")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time the matrix-core stream (tg_mfma_ceiling) on the workload's A and B "
+                         "and on zeros, for both MFMA shapes; one JSON line")
+    ap.add_argument("--ceiling-iters", type=int, default=1024,
+                    help="loop iterations per ceiling launch (2^20 flop per wave each)")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and print a table on stderr")
     ap.add_argument("--dtype", choices=["f16", "bf16", "mxf8"], default="f16",
@@ -365,7 +441,16 @@ def main() -> int:
                     help="GEMM FETCH_SIZE, GEMM WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE "
                          "counter_collection.csv files -> profiles/*__traffic.json")
     ap.add_argument("--traffic-kernel", default=None, help="kernel name for --traffic-record")
+    ap.add_argument("--trace-summary", metavar="CSV", default=None,
+                    help="print the per-call durations of the GEMM dispatches in a rocprofv3 "
+                         "kernel_trace.csv (with --steps/--warmup: the mean over the timed calls)")
+    ap.add_argument("--trace-kernel", default="gemm_", help="kernel name part for --trace-summary")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        t = trace_summary(args.trace_summary, args.trace_kernel, (args.warmup, args.warmup + args.steps))
+        print(json.dumps(t))
+        return 0
 
     if args.traffic_record:
         if not args.copy_bytes or not args.traffic_kernel:
@@ -390,6 +475,9 @@ def main() -> int:
         return 1
     w = workloads.BY_NAME[args.workload]
 
+    if args.mfma_ceiling:
+        return mfma_ceiling(w, args)
+
     if args.all:
         pk = PEAK_FP8_TFLOPS if args.dtype == "mxf8" else PEAK_FP16_TFLOPS
         log(f"{'workload':28s} {'kernel':32s} {'us':>9s} {'TFLOP/s':>9s} {'%peak':>7s} {'GB/s':>8s}")
@@ -402,10 +490,15 @@ def main() -> int:
             tf = ww.flop / (r["ms"] * 1e-3) / 1e12
             gbs = algorithmic_bytes(ww, args.dtype) / (r["ms"] * 1e-3) / 1e9
             pc = r["per_call_us"]
+            cpu_txt = ""
+            if not args.no_cpu_baseline:
+                c = cpu_baseline(ww, r["a"], r["b"], min(args.cpu_seconds, args.all_cpu_seconds), None,
+                                 args.dtype)
+                cpu_txt = f"  oracle {c['value'] * 1e3:.2f} GFLOP/s on {c['cores']} threads ({c['sample']})"
             log(f"{ww.name:28s} {r['kernel']:32s} {r['ms'] * 1e3:9.2f} {tf:9.1f} "
                 f"{100 * tf / pk:7.2f} {gbs:8.0f}"
                 + (f"  per call: median {pc['median']:.2f} min {pc['min']:.2f} "
-                   f"IQR {pc['p25']:.2f}-{pc['p75']:.2f} us" if pc else ""))
+                   f"IQR {pc['p25']:.2f}-{pc['p75']:.2f} us" if pc else "") + cpu_txt)
             if args.vendor and args.dtype != "mxf8":
                 v = time_workload(ww, args.steps, args.warmup, vendor=True, dtype=args.dtype,
                                   records=max(1, args.records))

@@ -23,7 +23,7 @@ import os
 __all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_ERR_TOO_LARGE",
            "TG_ERR_LAYOUT", "tg_gemm_mxf8", "tg_gemm_mxf8_plan",
            "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_gemm_bf16",
-           "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "gemm"]
+           "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "tg_mfma_ceiling", "gemm"]
 
 TG_OK = 0
 TG_ERR_INVALID_ARG = -1
@@ -72,6 +72,9 @@ def load():
     lib.tg_gemm_mxf8_plan.argtypes = [vp] * 5 + [i64] * 8 + [ctypes.c_char_p, i64, ctypes.POINTER(i64)]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_status_string.argtypes = [ctypes.c_int]
+    lib.tg_mfma_ceiling.restype = ctypes.c_int
+    lib.tg_mfma_ceiling.argtypes = [ctypes.c_int, vp, i64, vp, i64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, vp, vp]
     lib.tg_device_info.restype = ctypes.c_int
     lib.tg_device_info.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                    ctypes.c_char_p, i64]
@@ -142,6 +145,14 @@ def tg_gemm_mxf8_plan(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldsa: i
     return st, buf.value.decode(), tiles.value
 
 
+def tg_mfma_ceiling(shape: int, A, a_elems: int, B, b_elems: int, waves_per_simd: int, iters: int,
+                    workgroups: int, out, stream=None) -> int:
+    """Enqueue one launch of the matrix-core stream (measurement only; see
+    include/tg_ceiling.h); returns the C status code."""
+    return load().tg_mfma_ceiling(shape, _ptr(A), a_elems, _ptr(B), b_elems, waves_per_simd, iters,
+                                  workgroups, _ptr(out), _stream(stream))
+
+
 def tg_status_string(status: int) -> str:
     return load().tg_status_string(status).decode()
 
@@ -155,14 +166,19 @@ def tg_device_info():
 
 
 def gemm(A, B, out=None, stream=None):
-    """torch convenience: D = A·Bᵀ for fp16 or bf16 CUDA tensors A (M×K) and
-    B (N×K) of the same dtype whose last dimension is contiguous; D has that
-    dtype.  Uses torch's current stream when ``stream`` is None.  Raises
-    TgError on a non-zero status."""
+    """torch convenience: D = A·Bᵀ for fp16 or bf16 GPU tensors A (M×K) and
+    B (N×K) of the same dtype on one device, whose last dimension is
+    contiguous and whose row stride is at least the row length (K for A and
+    B, N for ``out``); D has that dtype.  Uses torch's current stream when
+    ``stream`` is None.  Raises TypeError / ValueError on tensors the C ABI
+    cannot take as they are (CPU tensors, mixed devices, overlapping rows such
+    as a stride-0 ``expand``) and TgError on a non-zero status."""
     import torch
 
     if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
         raise TypeError("A and B must both be float16 or both bfloat16")
+    if not A.is_cuda or not B.is_cuda or B.device != A.device:
+        raise ValueError("A and B must be GPU tensors on the same device")
     dt = A.dtype
     call = tg_gemm_f16 if dt == torch.float16 else tg_gemm_bf16
     if A.dim() != 2 or B.dim() != 2 or A.stride(1) != 1 or B.stride(1) != 1:
@@ -175,12 +191,22 @@ def gemm(A, B, out=None, stream=None):
         out = torch.empty((M, N), dtype=dt, device=A.device)
     elif out.dtype != dt or out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
         raise ValueError(f"out must be a {dt} (M, N) tensor with a contiguous last dimension")
-    if stream is None:
-        stream = torch.cuda.current_stream(A.device)
+    elif not out.is_cuda or out.device != A.device:
+        raise ValueError("out must be on the device of A and B")
+    # A row stride below the row length would make rows overlap (a stride-0
+    # expand, for instance); the kernels read and write whole rows at the
+    # given stride, so such views are refused rather than widened.  With one
+    # row the stride is never used.
+    for name, t, rows, width in (("A", A, M, K), ("B", B, N, K), ("out", out, M, N)):
+        if rows > 1 and t.stride(0) < width:
+            raise ValueError(f"{name} has row stride {t.stride(0)} < row length {width}; "
+                             "pass a tensor with non-overlapping rows (e.g. .contiguous())")
     lda = A.stride(0) if M > 1 else max(K, 1)
     ldb = B.stride(0) if N > 1 else max(K, 1)
     ldd = out.stride(0) if M > 1 else max(N, 1)
-    st = call(A, B, out, M, N, K, max(lda, K), max(ldb, K), max(ldd, N), stream)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    st = call(A, B, out, M, N, K, lda, ldb, ldd, stream)
     if st != TG_OK:
         raise TgError(st, call.__name__)
     return out

@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtg_gemm.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "tg_gemm.hip"), os.path.join(CSRC, "tile_layout_abi.cpp")]
+SOURCES = [os.path.join(CSRC, "tg_gemm.hip"), os.path.join(CSRC, "tg_ceiling.hip"),
+           os.path.join(CSRC, "tile_layout_abi.cpp")]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

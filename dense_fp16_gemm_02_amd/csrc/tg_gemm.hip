@@ -409,6 +409,15 @@ __device__ inline void wait_vmem()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// This lane's index in its wave, computed from the execution mask rather
+// than from the work-item id.  The epilogues call it after the K loop, so
+// that no register has to carry a lane-derived value across the loop (with
+// every VGPR of the loop taken, such values were spilled to scratch).
+__device__ inline int lane_id()
+{
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
 // Workgroup barrier that waits only for this wave's LDS reads (lgkmcnt), not
 // for its in-flight DMAs as __syncthreads would; the memory clobber keeps
 // the compiler from moving LDS accesses across it.
@@ -1474,7 +1483,8 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     auto stage_off = [](int r, int chunk) { return r * SROW + ((chunk ^ (r & (SCH - 1))) << 3); };
     barrier_lds();
     E *stg = reinterpret_cast<E *>(smem) + wave * WTM * WTN;
-    const int frag_row = frag_row_of(lane), frag_hi = frag_hi_of(lane);
+    const int elane = lane_id();
+    const int frag_row = frag_row_of(elane), frag_hi = frag_hi_of(elane);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1489,7 +1499,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
                 const int c = j * 32 + g * 8 + frag_hi * 4;
                 *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
             }
-    store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
+    store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, elane);
 }
 
 // 64×128 tiles of the block-scaled GEMM, for small M (M <= 64: one 64-row
@@ -1813,9 +1823,6 @@ constexpr const char *PATH_SUFFIX[3] = {"_dma", "_vec", "_scalar"};
 #ifndef TG_K_ON
 #define TG_K_ON 1
 #endif
-#ifndef TG_K2_WM
-#define TG_K2_WM 2
-#endif
 #ifndef TG_K2_STAGES
 #define TG_K2_STAGES 4
 #endif
@@ -1832,7 +1839,10 @@ constexpr const char *PATH_SUFFIX[3] = {"_dma", "_vec", "_scalar"};
 #define TG_K_MAXM 256
 #endif
 constexpr const char *TILE_STRIP64 = TG_TILE(64, TG_K_BN, 1, TG_K_WN);
-constexpr const char *TILE_STRIP128 = TG_TILE(128, 128, TG_K2_WM, 4 / TG_K2_WM);
+// The 128×128 column strip shares its tile and wave grid with the general
+// 128×128 tile; its name says "strip" so that the two instantiations (K
+// rotation and streaming B here) stay apart in plans and profiles.
+constexpr const char *TILE_STRIP128 = TG_TILE(128, 128, 2, 2) "_strip";
 constexpr const char *TILE_STRIP256 = TG_TILE(256, 128, 2, 2);
 constexpr const char *TILE_256 = TG_TILE(256, 256, 2, 2);
 constexpr const char *TILE_128 = TG_TILE(128, 128, 2, 2);
@@ -1880,7 +1890,7 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
         k = choice<E, 64, TG_K_BN, 1, TG_K_WN, TG_K_BK, TG_K_STAGES, TG_K_DS, 1, 1>(
             path(64, TG_K_BN), TILE_STRIP64);
     else if (TG_K_ON && M <= 128 && TG_K_MAXM >= 128 && tiles(128, 128) >= NUM_CU / 2)
-        k = choice<E, 128, 128, TG_K2_WM, 4 / TG_K2_WM, TG_K2_BK, TG_K2_STAGES, 2, 1, 1>(
+        k = choice<E, 128, 128, 2, 2, TG_K2_BK, TG_K2_STAGES, 2, 1, 1>(
             path(128, 128), TILE_STRIP128);
     else if (TG_K_ON && M <= 256 && TG_K_MAXM >= 256 && tiles(256, 128) >= NUM_CU / 2)
         k = choice<E, 256, 128, 2, 2, TG_K4_BK, TG_K4_STAGES, 2, 1, 1>(path(256, 128), TILE_STRIP256);
@@ -2014,11 +2024,15 @@ extern "C" int tg_gemm_bf16_plan(const void *A, const void *B, const void *D, in
 // workgroup, or one 64×128 tile per workgroup where M <= 64 and N gives at
 // least 128 column strips (HBM-bound: B streams once) or where the problem
 // has too few 256×256 tiles to occupy a quarter of the GPU.
-constexpr const char *MXF8_KERNEL = "gemm_mxf8_256x256_w2x2_dma";
+// The 256×256 kernel loads scale words in groups of four K-tiles when four
+// divide the K-tile count, else in pairs: two instantiations, two names.
+constexpr const char *MXF8_KERNEL_G4 = "gemm_mxf8_256x256_w2x2_g4_dma";
+constexpr const char *MXF8_KERNEL_G2 = "gemm_mxf8_256x256_w2x2_g2_dma";
 constexpr const char *MXF8_STRIP_KERNEL = "gemm_mxf8_64x128_w1x4_dma";
 #ifndef TG_MX_STRIP_STAGES
 #define TG_MX_STRIP_STAGES 4
 #endif
+bool mx_group4(int64_t K) { return ((K + 127) / 128) % 4 == 0; }
 bool mx_uses_strip(int64_t M, int64_t N)
 {
     return (M <= 64 && (N + 127) / 128 >= NUM_CU / 2) || ((M + 255) / 256) * ((N + 255) / 256) < NUM_CU / 4;
@@ -2076,8 +2090,7 @@ extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const 
                     &lda, &ldsa, &ldb, &ldsb, &ldd, &tiles_m, &tiles_n, &dvec};
     // groups of four K-tiles when they divide the K-tile count, else pairs
     // (at most one padding K-tile)
-    const int64_t kt = (K + 127) / 128;
-    const void *fn = kt % 4 == 0 ? reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 4>)
+    const void *fn = mx_group4(K) ? reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 4>)
                                  : reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 2>);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
@@ -2097,7 +2110,8 @@ extern "C" int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, c
         return st;
     const bool strip = mx_uses_strip(M, N);
     if (name && name_len > 0)
-        snprintf(name, (size_t)name_len, "%s", strip ? MXF8_STRIP_KERNEL : MXF8_KERNEL);
+        snprintf(name, (size_t)name_len, "%s",
+                 strip ? MXF8_STRIP_KERNEL : mx_group4(K) ? MXF8_KERNEL_G4 : MXF8_KERNEL_G2);
     if (tiles)
         *tiles = strip ? mx_strip_tiles(M, N) : ((M + 255) / 256) * ((N + 255) / 256);
     return TG_OK;

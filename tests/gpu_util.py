@@ -74,3 +74,30 @@ def guard_intact(full: np.ndarray, M: int, N: int, guard: int) -> bool:
     mask = np.ones(full.shape, dtype=bool)
     mask[guard:guard + M, guard:guard + N] = False
     return bool(np.all(full[mask] == SENTINEL))
+
+
+def _bytes(x: np.ndarray):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to("cuda:0")
+
+
+def run_mx(a, sa, b, sb, M, N, K, guard=0, label=""):
+    """D (M, N) fp16 window and the full (M+2g, N+2g) buffer (uint16) of
+    tg_gemm_mxf8 on byte arrays a (M, lda), sa (M, ldsa), b (N, ldb), sb
+    (N, ldsb); every byte in them is passed to the device as is."""
+    import torch
+
+    import dense_fp16_gemm_02_amd as tg
+
+    lda, ldsa, ldb, ldsb = a.shape[1], sa.shape[1], b.shape[1], sb.shape[1]
+    ldd = N + 2 * guard
+    A, SA, B, SB = _bytes(a), _bytes(sa), _bytes(b), _bytes(sb)
+    d = torch.full(((M + 2 * guard) * ldd + 8,), SENTINEL, dtype=torch.int16, device="cuda:0")
+    dptr = d.data_ptr() + 2 * (guard * ldd + guard)
+    say(f"mxf8 {label} M={M} N={N} K={K} lda={lda} ldsa={ldsa} ldb={ldb} ldsb={ldsb} guard={guard}")
+    st = tg.tg_gemm_mxf8(A, SA, B, SB, dptr, M, N, K, lda, ldsa, ldb, ldsb, ldd, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    full = d.cpu().numpy().view(np.uint16)[:(M + 2 * guard) * ldd].reshape(M + 2 * guard, ldd)
+    win = np.array(full[guard:guard + M, guard:guard + N].view(np.float16))
+    return win, full, st

@@ -147,20 +147,21 @@ def test_mxf8_plans_and_validation():
             assert st == tg.TG_OK and name == "gemm_mxf8_64x128_w1x4_dma"
             assert tiles == ((w.M + 63) // 64) * ((w.N + 127) // 128)
         else:
-            assert st == tg.TG_OK and name == "gemm_mxf8_256x256_w2x2_dma"
+            group = "g4" if ((w.K + 127) // 128) % 4 == 0 else "g2"
+            assert st == tg.TG_OK and name == f"gemm_mxf8_256x256_w2x2_{group}_dma"
             assert tiles == ((w.M + 255) // 256) * ((w.N + 255) // 256)
     # the strip needs M <= 64 and at least 128 strips
     assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 16384, 128, 128, 4, 128, 4, 16384)[1] == \
         "gemm_mxf8_64x128_w1x4_dma"
     assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 16384, 128, 128, 4, 128, 4, 16384)[1] == \
-        "gemm_mxf8_256x256_w2x2_dma"
+        "gemm_mxf8_256x256_w2x2_g2_dma"
     assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 16256, 128, 128, 4, 128, 4, 16256)[1] == \
-        "gemm_mxf8_256x256_w2x2_dma"
+        "gemm_mxf8_256x256_w2x2_g2_dma"
     # and problems with fewer than 64 tiles of 256x256 take 64x128 tiles
     assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 1792, 128, 128, 4, 128, 4, 1792)[1:] == \
         ("gemm_mxf8_64x128_w1x4_dma", 32 * 14)
     assert tg.tg_gemm_mxf8_plan(FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 2048, 128, 128, 4, 128, 4, 2048)[1] == \
-        "gemm_mxf8_256x256_w2x2_dma"
+        "gemm_mxf8_256x256_w2x2_g2_dma"
     ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 128, 128, 4, 128, 4, 64)
     assert tg.tg_gemm_mxf8_plan(*ok)[0] == tg.TG_OK
 
@@ -187,3 +188,14 @@ def test_mxf8_plans_and_validation():
     assert tg.tg_gemm_mxf8(None, None, None, None, None, 0, 0, 0, 0, 0, 0, 0, 0, None) == tg.TG_OK
     assert tg.tg_gemm_mxf8_plan(None, None, FAKE, FAKE, None, 0, 7, 64, 64, 4, 64, 4, 7) == (tg.TG_OK, "", 0)
     assert tg.tg_status_string(tg.TG_ERR_LAYOUT) != "unknown status"
+
+
+def test_torch_wrapper_refuses_cpu_tensors():
+    """gemm() hands device pointers to the kernels: host tensors are refused
+    before any call reaches the library."""
+    torch = pytest.importorskip("torch")
+    A = torch.zeros(4, 8, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        tg.gemm(A, A)
+    with pytest.raises(TypeError):
+        tg.gemm(A, A.float())

@@ -73,3 +73,20 @@ def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
     assert bench.main() == 2
     assert "one GPU" in capsys.readouterr().err
 
+
+
+def test_trace_summary_orders_dispatches_and_averages_the_timed_window(tmp_path):
+    """The per-call series comes out in start order (not file order) and the
+    window mean covers exactly the timed calls [warmup, warmup + steps)."""
+    p = tmp_path / "kernel_trace.csv"
+    starts = [500, 100, 300, 700, 900]
+    durs_ns = [5000, 1000, 3000, 7000, 9000]  # by start order: 1, 3, 5, 7, 9 us
+    with open(p, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        for s0, d in zip(starts, durs_ns):
+            wr.writerow({"Kernel_Name": "gemm_x", "Start_Timestamp": s0, "End_Timestamp": s0 + d})
+        wr.writerow({"Kernel_Name": "copyBuffer", "Start_Timestamp": 50, "End_Timestamp": 99999})
+    t = bench.trace_summary(str(p), "gemm_", (1, 4))
+    assert t["per_call_us"] == [1.0, 3.0, 5.0, 7.0, 9.0]
+    assert t["calls"] == 5 and t["window_mean_us"] == 5.0 and t["mean_us"] == 5.0

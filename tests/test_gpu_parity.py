@@ -200,20 +200,20 @@ def test_large_tile_tails():
 
 
 @pytest.mark.parametrize("M,N,K,tile", [
-    (64, 16411, 1000, "64x128"),    # full strip, ragged N and K
-    (37, 16400, 200, "64x128"),     # ragged M; K spans 4 K-tiles (start offsets wrap)
-    (1, 16385, 64, "64x128"),       # one row; one K-tile
-    (100, 16390, 776, "128x128"),
-    (128, 16384, 1024, "128x128"),
-    (200, 16500, 512, "256x128"),
-    (256, 16384, 264, "256x128"),
+    (64, 16411, 1000, "64x128_w1x4"),    # full strip, ragged N and K
+    (37, 16400, 200, "64x128_w1x4"),     # ragged M; K spans 4 K-tiles (start offsets wrap)
+    (1, 16385, 64, "64x128_w1x4"),       # one row; one K-tile
+    (100, 16390, 776, "128x128_w2x2_strip"),
+    (128, 16384, 1024, "128x128_w2x2_strip"),
+    (200, 16500, 512, "256x128_w2x2"),
+    (256, 16384, 264, "256x128_w2x2"),
 ])
 def test_strip_tiles(M, N, K, tile):
     """Small M and large N take the column-strip tiles (one tile row covers
     M, each XCD starts at its own K offset); every element is checked."""
     st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N + 2)
     say(f"strip plan {name} tiles={tiles}")
-    assert st0 == tg.TG_OK and name.startswith(f"gemm_f16_{tile}_") and name.endswith("_dma")
+    assert st0 == tg.TG_OK and name == f"gemm_f16_{tile}_dma"
     a = workloads.random_f16(300 + M, (M, K))
     b = workloads.random_f16(400 + K, (N, K))
     d, full, st = run(a, b, M, N, K, guard=1, label=f"strip {name}")
@@ -344,3 +344,27 @@ def test_torch_wrapper_matches():
     torch.cuda.synchronize()
     res = oracle.gemm(A.cpu().numpy(), B.cpu().numpy(), 333, 444, 256)
     _check(D.cpu().numpy(), res, "wrapper")
+
+
+def test_torch_wrapper_refuses_overlapping_rows_and_mixed_devices():
+    """A row stride below the row length (a stride-0 expand) would make the
+    kernel read K·M elements from a K-element buffer: refused, not widened;
+    so are operands on another device."""
+    x = torch.randn(1, 64, device="cuda:0").half()
+    B = torch.randn(32, 64, device="cuda:0").half()
+    with pytest.raises(ValueError, match="row stride"):
+        tg.gemm(x.expand(16, 64), B)
+    with pytest.raises(ValueError, match="row stride"):
+        tg.gemm(B, x.expand(16, 64))
+    out = torch.empty(1, 16, device="cuda:0").half().expand(32, 16)
+    with pytest.raises(ValueError, match="row stride"):
+        tg.gemm(B, x.expand(16, 64).contiguous(), out=out)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        tg.gemm(B, B.cpu())
+    with pytest.raises(ValueError, match="device"):
+        tg.gemm(B, B, out=torch.empty(32, 32, dtype=torch.float16))
+    # a single row never uses its stride: an expanded one-row view is fine
+    D = tg.gemm(x.expand(1, 64), B)
+    torch.cuda.synchronize()
+    res = oracle.gemm(x.cpu().numpy(), B.cpu().numpy(), 1, 32, 64)
+    _check(D.cpu().numpy(), res, "one-row wrapper")

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import SENTINEL, say
+from gpu_util import SENTINEL, run_mx, say
 
 torch = pytest.importorskip("torch")
 tg = pytest.importorskip("dense_fp16_gemm_02_amd")
@@ -31,27 +31,6 @@ def _device():
         pytest.skip("no GPU")
     tg.load()
     torch.cuda.init()
-
-
-def _bytes(x: np.ndarray):
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to("cuda:0")
-
-
-def run_mx(a, sa, b, sb, M, N, K, guard=0, label=""):
-    """D (M, N) fp16 window and the full (M+2g, N+2g) buffer (uint16) of
-    tg_gemm_mxf8 on byte arrays a (M, lda), sa (M, ldsa), b (N, ldb), sb
-    (N, ldsb); every byte in them is passed to the device as is."""
-    lda, ldsa, ldb, ldsb = a.shape[1], sa.shape[1], b.shape[1], sb.shape[1]
-    ldd = N + 2 * guard
-    A, SA, B, SB = _bytes(a), _bytes(sa), _bytes(b), _bytes(sb)
-    d = torch.full(((M + 2 * guard) * ldd + 8,), SENTINEL, dtype=torch.int16, device="cuda:0")
-    dptr = d.data_ptr() + 2 * (guard * ldd + guard)
-    say(f"mxf8 {label} M={M} N={N} K={K} lda={lda} ldsa={ldsa} ldb={ldb} ldsb={ldsb} guard={guard}")
-    st = tg.tg_gemm_mxf8(A, SA, B, SB, dptr, M, N, K, lda, ldsa, ldb, ldsb, ldd, torch.cuda.current_stream())
-    torch.cuda.synchronize()
-    full = d.cpu().numpy().view(np.uint16)[:(M + 2 * guard) * ldd].reshape(M + 2 * guard, ldd)
-    win = np.array(full[guard:guard + M, guard:guard + N].view(np.float16))
-    return win, full, st
 
 
 def _guard_ok(full, M, N, g):
@@ -75,7 +54,8 @@ def _ld4(n):
 
 
 STRIP = "gemm_mxf8_64x128_w1x4_dma"
-BIG = "gemm_mxf8_256x256_w2x2_dma"
+BIG = "gemm_mxf8_256x256_w2x2_g2_dma"    # scale words in pairs of K-tiles
+BIG4 = "gemm_mxf8_256x256_w2x2_g4_dma"   # ... in groups of four (4 divides the K-tile count)
 
 
 def _plan_name(M, N, K, lda, ldsa, ldb, ldsb, ldd):
@@ -117,7 +97,8 @@ def _pm1(seed, rows, K):
 
 
 @pytest.mark.parametrize("M,N,K,kernel", [(256, 256, 128, STRIP), (300, 520, 256, STRIP), (77, 600, 1024, STRIP),
-                                          (513, 129, 96, STRIP), (2100, 2050, 128, BIG), (2049, 2100, 96, BIG)])
+                                          (513, 129, 96, STRIP), (2100, 2050, 128, BIG), (2049, 2100, 96, BIG),
+                                          (2100, 2050, 512, BIG4)])
 def test_unit_scales_exact(M, N, K, kernel):
     """Values in {-1, 0, 1} with unit scales: D is an integer ≤ K, exact in
     fp32 and fp16, so every element must match the oracle bit for bit (on
@@ -134,10 +115,11 @@ def test_unit_scales_exact(M, N, K, kernel):
 
 
 @pytest.mark.parametrize("M,N,K,kernel", [(256, 256, 256, STRIP), (190, 333, 384, STRIP), (260, 260, 96, STRIP),
-                                          (2100, 2060, 256, BIG), (2070, 2090, 96, BIG)])
+                                          (2100, 2060, 256, BIG), (2070, 2090, 96, BIG),
+                                          (2080, 2100, 1536, BIG4)])
 def test_random_scales_exact(M, N, K, kernel):
     """Values ±1 and 0 with scales 2^-3..2^3 per block: every partial sum is a
-    multiple of 2^-6 below 2^12, exact in fp32, so D is bit-exact.  A scale
+    multiple of 2^-6 below 2^17 (K <= 1536), exact in fp32, so D is bit-exact.  A scale
     applied to the wrong block, lane half or operand changes D."""
     a, b = _pm1(21 + K, M, K), _pm1(22 + K, N, K)
     rng = np.random.default_rng(23 + K)

@@ -1,0 +1,66 @@
+"""Host-only checks that the GPU coverage table names every kernel the
+planners can choose (no device is touched: the plan entry points only
+validate and choose).
+
+1. Every case of ``planner_cases`` plans to the name it is filed under.
+2. A sweep over the planners' inputs — shape classes around every tile
+   threshold, tight and huge row strides, aligned and misaligned pointers,
+   K multiple of 8 or not — returns only names that are in the table, and
+   reaches every name the table holds.
+"""
+import itertools
+
+import pytest
+
+from planner_cases import CASES, MX_CASES, all_fp_names, vec_lda
+
+tg = pytest.importorskip("dense_fp16_gemm_02_amd")
+
+BASE = 1 << 20  # a 16-byte aligned fake device address (plans never dereference)
+
+
+def _plan(fmt, M, N, K, lda, ldb, a_off=0):
+    plan = tg.tg_gemm_bf16_plan if fmt == "bf16" else tg.tg_gemm_f16_plan
+    st, name, tiles = plan(BASE + 2 * a_off, BASE, BASE, M, N, K, lda, ldb, N)
+    assert st == tg.TG_OK
+    return name
+
+
+def test_every_case_plans_to_its_name():
+    for name, (fmt, c) in CASES.items():
+        lda, ldb = c.lds()
+        assert _plan(fmt, c.M, c.N, c.K, lda, ldb, c.a_off) == name, (name, c)
+    for name, c in MX_CASES.items():
+        nb = c.K // 32
+        ld = max(4, (nb + 3) // 4 * 4)
+        st, got, _ = tg.tg_gemm_mxf8_plan(BASE, BASE, BASE, BASE, BASE, c.M, c.N, c.K, c.K, ld, c.K, ld, c.N)
+        assert st == tg.TG_OK and got == name, (name, c)
+
+
+def test_table_is_exactly_the_planner_universe():
+    assert set(CASES) == all_fp_names()
+
+
+def test_planner_sweep_stays_inside_the_table():
+    Ms = [1, 2, 37, 64, 65, 100, 128, 129, 200, 256, 257, 1000, 2100, 4100]
+    Ns = [131, 300, 2000, 5120, 16256, 16385, 16411, 40960]
+    seen = set()
+    for fmt, M, N in itertools.product(("f16", "bf16"), Ms, Ns):
+        for K, a_off in ((64, 0), (200, 0), (250, 0), (96, 1)):
+            for lda in (K, vec_lda(256), vec_lda(128), vec_lda(64)):
+                name = _plan(fmt, M, N, K, lda, K, a_off)
+                assert name in CASES, (fmt, M, N, K, lda, a_off, name)
+                seen.add(name)
+    assert seen == set(CASES), sorted(set(CASES) - seen)
+
+
+def test_mx_planner_sweep_stays_inside_the_table():
+    seen = set()
+    for M, N, K in itertools.product([1, 64, 65, 300, 2048, 2100, 8192], [600, 2060, 16256, 16400, 28672],
+                                     [32, 128, 384, 512, 4096, 4192]):
+        nb = K // 32
+        ld = max(4, (nb + 3) // 4 * 4)
+        st, name, _ = tg.tg_gemm_mxf8_plan(BASE, BASE, BASE, BASE, BASE, M, N, K, K, ld, K, ld, N)
+        assert st == tg.TG_OK and name in MX_CASES, (M, N, K, name)
+        seen.add(name)
+    assert seen == set(MX_CASES)
