@@ -434,7 +434,9 @@ def main() -> int:
                     help="element type (the headline metric is fp16; bf16 and block-scaled FP8 "
                          "are reported alongside)")
     ap.add_argument("--vendor", action="store_true",
-                    help="with --all: also time torch.matmul on the same inputs (context)")
+                    help="with --all: also time torch.matmul on the same inputs (context); without "
+                         "--all: the line times torch.matmul instead of this library (context only, "
+                         "config.kernel says so)")
     ap.add_argument("--copy-bytes", type=int, default=None,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--traffic-record", nargs=4, metavar="CSV", default=None,
@@ -506,8 +508,11 @@ def main() -> int:
                 log(f"{'':28s} {'torch.matmul':32s} {v['ms'] * 1e3:9.2f} {tfv:9.1f} "
                     f"{100 * tfv / PEAK_FP16_TFLOPS:7.2f} {ww.min_bytes / (v['ms'] * 1e-3) / 1e9:8.0f}")
 
+    vendor_line = args.vendor and not args.all and args.dtype != "mxf8"
     r = time_workload(w, args.steps, args.warmup, dtype=args.dtype, records=max(1, args.records),
-                      per_call=args.per_call)
+                      per_call=args.per_call, vendor=vendor_line)
+    if vendor_line:
+        r["kernel"] = "torch.matmul (vendor library; context only)"
     ms = r["ms"]
     tflops = w.flop / (ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if args.dtype == "mxf8" else PEAK_FP16_TFLOPS

@@ -73,12 +73,17 @@ __global__ __launch_bounds__(256) void mfma_stream_kernel(const _Float16 *__rest
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     acc[i][j][v] = 0.0f;
+        // two passes over the 16 accumulators: 32 MFMAs of 2^15 flop, the
+        // same 2^20 flop per iteration as the 16x16x32 form
         for (int it = 0; it < iters; ++it) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int pass = 0; pass < 2; ++pass)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[(i + pass) & 3], acc[i][j],
+                                                                           0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)

@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -133,8 +134,10 @@ constexpr int NUM_XCD = 8;
 #endif
 constexpr int GROUP_M = TG_GROUP_M;
 
-__host__ __device__ constexpr void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+template <int GM>
+__host__ __device__ constexpr void tile_of_grouped(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
 {
+    constexpr int GROUP_M = GM;
     const int total = tiles_m * tiles_n;
     const int xcd = bid % NUM_XCD;
     const int local = bid / NUM_XCD;
@@ -156,8 +159,14 @@ __host__ __device__ constexpr void tile_of(int bid, int tiles_m, int tiles_n, in
         tn -= tiles_n;
 }
 
+__host__ __device__ constexpr void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    tile_of_grouped<GROUP_M>(bid, tiles_m, tiles_n, tm, tn);
+}
+
 // Every workgroup id in [0, tiles_m·tiles_n) maps to a distinct tile inside
 // the grid (checked at compile time on shapes with and without remainders).
+template <int GM = GROUP_M>
 constexpr bool tile_order_is_bijective(int tiles_m, int tiles_n)
 {
     bool seen[4096] = {};
@@ -165,7 +174,7 @@ constexpr bool tile_order_is_bijective(int tiles_m, int tiles_n)
         return false;
     for (int b = 0; b < tiles_m * tiles_n; ++b) {
         int tm = -1, tn = -1;
-        tile_of(b, tiles_m, tiles_n, tm, tn);
+        tile_of_grouped<GM>(b, tiles_m, tiles_n, tm, tn);
         if (tm < 0 || tm >= tiles_m || tn < 0 || tn >= tiles_n || seen[tm * tiles_n + tn])
             return false;
         seen[tm * tiles_n + tn] = true;
@@ -178,6 +187,11 @@ static_assert(tile_order_is_bijective(32, 56) && tile_order_is_bijective(16, 16)
                   tile_order_is_bijective(3, 1) && tile_order_is_bijective(13, 5) &&
                   tile_order_is_bijective(9, 17) && tile_order_is_bijective(64, 64),
               "workgroup → tile order must cover every tile exactly once");
+static_assert(tile_order_is_bijective<8>(32, 56) && tile_order_is_bijective<8>(16, 16) &&
+                  tile_order_is_bijective<8>(1, 448) && tile_order_is_bijective<8>(7, 9) &&
+                  tile_order_is_bijective<8>(17, 33) && tile_order_is_bijective<8>(9, 17) &&
+                  tile_order_is_bijective<8>(64, 64) && tile_order_is_bijective<8>(3, 1),
+              "workgroup → tile order (groups of 8 tile rows) must cover every tile exactly once");
 
 // One 16-byte chunk (8 consecutive K) of row `row` of a K-major operand,
 // zero outside rows [0,rows) or K.  VEC: 16-byte aligned rows with K % 8 == 0,
@@ -1127,6 +1141,316 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
     store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
 }
 
+// Persistent form of the 256×256 kernel (the pages' Step 6: a fixed pool of
+// workgroups, each taking tile after tile — "TIRx 与高性能GEMM (上)",
+// section "Step 6：Persistent kernel 让 CTA 持续领取 tile").  One workgroup
+// per compute unit (the grid is a multiple of 8, so workgroup w stays on XCD
+// w mod 8); workgroup w takes the tiles of virtual ids w, w + P, w + 2P, ...
+// (P = grid size) through the same XCD-grouped order as the one-tile-per-
+// workgroup launch, so the tiles resident on an XCD at any moment are the
+// same ones.  K must be a multiple of 64 and at least 128 (no partial
+// K-tile; the next tile's first two K-tiles load during the last two).
+//
+// The K-tiles of a workgroup's tiles form one stream: the refills run two
+// K-tiles ahead of the matrix cores across tile boundaries, so the next
+// tile's first operand tiles are already landing while the current tile's
+// last K-tiles are multiplied, and no tile starts by waiting for its first
+// loads.  Rings: SA_ stages of A and 5 - SA_ of B (32 KiB each); the operand
+// with three stages is refilled in K-step 0 (two K-tiles of latency budget),
+// the other in K-step 1, after the barrier that drains its stage.
+//
+// Epilogue, at the last K-tile of a tile, with no workgroup barrier: the
+// 3-stage operand's stage of that K-tile is free until the next tile's
+// second K-step, and the 2-stage operand's refill is held back until the
+// epilogue is done, so both drained stages (64 KiB) hold the staging of
+// D.  Each wave stages its 128×128 block in two 64-row halves of 16 KiB, in
+// exactly the 1 KiB pieces of those two stages that its own DMAs fill (a
+// DMA instruction of wave w writes the piece 4p + w of a stage), so the
+// only later writers of its staging memory are its own DMAs, issued after
+// its own staging reads have completed.  Per half: fp32 → element RNE into
+// LDS (16-byte chunk index XORed with the row), read back 16 bytes per lane
+// along rows, store whole row segments; the accumulators are cleared as
+// they are read.  Then the held-back refill is issued and the next tile's
+// first K-step runs on fragments read before the epilogue.
+//
+// RS0: fragment reads of K-step 0 every RS0-th MFMA slot (2: in the first
+// half of the step, so they have landed by the barrier's wait; 4: spread).
+template <typename E, int SA_, int GM, int RS0>
+__global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
+    const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
+    int dvec)
+{
+    using V8 = typename Elem<E>::v8;
+    using V4 = typename Elem<E>::v4;
+    constexpr int BM = 256, BN = 256, WM = 2, WN = 2, MF = 16, BK_ = 64;
+    constexpr int SA = SA_, SB = 5 - SA_;
+    static_assert(SA == 2 || SA == 3, "three stages of one operand, two of the other");
+    using T = OperandTile<BK_>;
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / MF, TN = WTN / MF;
+    constexpr int CPK = 4;                               // 16-byte chunks per row per 32-K step
+    constexpr int PASSES = BM / T::ROWS_PER_DMA / NW;    // DMAs per wave per operand K-tile
+    constexpr int STAGE = BM * BK_;                      // elements of one operand stage (32 KiB)
+    constexpr int PIECE = T::ROWS_PER_DMA * BK_;         // elements one DMA instruction fills (1 KiB)
+    static_assert(BM == BN && PASSES == 8 && PIECE * 2 == 1024, "square tile, 1 KiB DMA pieces");
+    static_assert(STAGE == 4 * PASSES * PIECE, "a stage is 32 pieces, 8 per wave");
+    static_assert(PASSES <= 63, "vmcnt holds 6 bits");
+
+    __shared__ __attribute__((aligned(1024))) E smem[(SA + SB) * STAGE];
+    E *const a_ring = smem;
+    E *const b_ring = smem + SA * STAGE;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int P = (int)gridDim.x;
+    const int total = tiles_m * tiles_n;
+    const int mine = (total - (int)blockIdx.x + P - 1) / P;  // tiles of this workgroup (>= 1)
+    const int KT = K / BK_;  // at least 2
+
+    // Tile i of this workgroup.  The grid sizes go through an opaque copy so
+    // that the divisions of the tile order are done here, once per tile,
+    // instead of keeping their reciprocals in vector registers across the K
+    // loop.
+    auto my_tile = [&](int i, int &tm, int &tn) {
+        int gm = tiles_m, gn = tiles_n;
+        asm volatile("" : "+s"(gm), "+s"(gn));
+        tile_of_grouped<GM>((int)blockIdx.x + i * P, gm, gn, tm, tn);
+    };
+    // DMA sources: lane l of a wave fills physical chunk l mod 8 of row l / 8
+    // of its pieces; successive pieces of a wave are 32 rows apart (a whole
+    // number of swizzle periods), so its logical chunk kc is the same in all.
+    static_assert((NW * T::ROWS_PER_DMA) % 16 == 0, "swizzle repeats per pass");
+    uint32_t a_off[PASSES], b_off[PASSES];
+    const char *a_src = nullptr, *b_src = nullptr;  // tile origins of the DMA stream's tile
+    // Point the DMA stream at tile i of this workgroup: rows past M (N) are
+    // clamped to the last row (they feed only D rows that are never stored).
+    // The lane terms are recomputed here from an opaque lane index, so the
+    // compiler cannot hoist them out of the tile loop into registers that
+    // would have to live across the K loop.
+    auto set_dma_tile = [&](int i) {
+        int l = lane_id();
+        asm volatile("" : "+v"(l));
+        const int dr = l / T::RC;
+        const int kc = (l % T::RC) ^ T::swz(T::ROWS_PER_DMA * wave + dr);
+        int tm, tn;
+        my_tile(i, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        a_src = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
+        b_src = reinterpret_cast<const char *>(B + (int64_t)n0 * ldb);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int t = T::ROWS_PER_DMA * (p * NW + wave) + dr;
+            a_off[p] = (uint32_t)(imin(t, M - 1 - m0) * lda * 2 + 16 * kc);
+            b_off[p] = (uint32_t)(imin(t, N - 1 - n0) * ldb * 2 + 16 * kc);
+        }
+    };
+    // DMA stream: the refills run two K-tiles ahead of the matrix cores,
+    // into the next tile during the last two K-tiles of a tile.  dsa, dsb:
+    // the stages the next refills land in.
+    int dsa = 0, dsb = 0;
+    set_dma_tile(0);
+    // descriptor of K-tile dk of the DMA stream's tile (live: the tile
+    // exists; otherwise an empty range: every lane reads zero, no access)
+    auto dma_rsrc = [&](const char *src, int dk, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(src + 2 * (int64_t)dk * BK_), (short)0,
+                                                 live ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
+    };
+    auto next_dma_stage = [&]() {
+        dsa = dsa + 1 == SA ? 0 : dsa + 1;
+        dsb = dsb + 1 == SB ? 0 : dsb + 1;
+    };
+    auto dma_a = [&](__amdgpu_buffer_rsrc_t r, int p) {
+        dma16<CPOL_CACHED>(r, a_ring + dsa * STAGE + (p * NW + wave) * PIECE, a_off[p]);
+    };
+    auto dma_b = [&](__amdgpu_buffer_rsrc_t r, int p) {
+        dma16<CPOL_CACHED>(r, b_ring + dsb * STAGE + (p * NW + wave) * PIECE, b_off[p]);
+    };
+
+    const int frag_row = frag16_row_of(lane), frag_hi = frag16_hi_of(lane);
+    V8 fa[2][TM], fb[2][TN];
+    static_assert(T::swz(16) == T::swz(0) && WTM % 16 == 0 && WTN % 16 == 0, "swizzle period");
+    int a_lane[2], b_lane[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        a_lane[kk] = T::off(wm * WTM + frag_row, kk * CPK + frag_hi);
+        b_lane[kk] = T::off(wn * WTN + frag_row, kk * CPK + frag_hi);
+    }
+    auto read_frag = [&](int sa, int sb, int kk, int q, V8 *a, V8 *b) {
+        if (q < TM)
+            a[q] = *reinterpret_cast<const V8 *>(a_ring + sa * STAGE + a_lane[kk] + q * MF * BK_);
+        else
+            b[q - TM] = *reinterpret_cast<const V8 *>(b_ring + sb * STAGE + b_lane[kk] + (q - TM) * MF * BK_);
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    constexpr int NFRAG = TM + TN;
+    constexpr int SLOTS = TM * TN;
+    auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
+    // One K-step: MFMA per slot; the next step's fragment read i after MFMA
+    // RS·i; DMA pass (i-1)/8 of `which` (0: none, 1: A, 2: B) after every
+    // eighth odd slot.
+    auto step = [&](const V8 *a, const V8 *b, bool with_reads, int rsa, int rsb, int rkk, V8 *na, V8 *nb,
+                    int which, __amdgpu_buffer_rsrc_t r, auto rs_tag) {
+        constexpr int RS = decltype(rs_tag)::value;
+        static_assert(SLOTS / RS >= NFRAG && SLOTS % 8 == 0, "reads and DMAs fit the slots");
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int ti = i / TN, tj = i % TN;
+            acc[ti][tj] = Elem<E>::mfma(b[tj], a[ti], acc[ti][tj]);
+            MFMA_FIRST();
+            if (with_reads && i % RS == 0 && i / RS < NFRAG)
+                read_frag(rsa, rsb, rkk, frag_of_slot(i / RS), na, nb);
+            if (which && i % 8 == 1) {
+                if (which == 1)
+                    dma_a(r, i / 8);
+                else
+                    dma_b(r, i / 8);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using rs0_t = std::integral_constant<int, RS0>;
+    using rs4_t = std::integral_constant<int, 4>;
+    constexpr int X3 = SA == 3 ? 1 : 2;  // operand with three stages: refilled in K-step 0
+    constexpr int Y2 = 3 - X3;           // the other: refilled in K-step 1
+
+    // Staged epilogue of tile `ti`, using stage sa of A and stage sb of B.
+    auto epilogue = [&](int ti, int sa, int sb) __attribute__((always_inline)) {
+        int tm, tn;
+        my_tile(ti, tm, tn);
+        const int row0 = tm * BM + wm * WTM, col0 = tn * BN + wn * WTN;
+        E *const st_a = a_ring + sa * STAGE + wave * PIECE;  // this wave's pieces: +4·PIECE apart
+        E *const st_b = b_ring + sb * STAGE + wave * PIECE;
+        // piece q (0..15) of the half: rows 4q..4q+3, 256 bytes each
+        auto piece = [&](int q) { return q < 8 ? st_a + q * 4 * PIECE : st_b + (q - 8) * 4 * PIECE; };
+        int l = lane_id();
+        asm volatile("" : "+v"(l));  // opaque: the lane terms below are not hoisted out of the tile loop
+        const int fr = l & 15, fh = l >> 4;     // accumulator lane: D row fr, columns 4·fh..4·fh+3
+        const int rr = l >> 4, rc = l & 15;     // store lane: row rr of a piece, 16-byte chunk rc
+        const bool inside = dvec && row0 + WTM <= M && col0 + WTN <= N;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < TM / 2; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const f32x4 v = acc[4 * h + i][j];
+                    acc[4 * h + i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    V4 e;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        e[r] = (E)v[r];  // round to nearest even
+                    const int c = j * MF + 4 * fh;  // column in the wave block
+                    E *dst = piece(4 * i + (fr >> 2)) + (fr & 3) * (WTN) + (((c >> 3) ^ fr) << 3) + (c & 7);
+                    *reinterpret_cast<V4 *>(dst) = e;
+                }
+            const int rbase = row0 + 64 * h;
+            const int col = col0 + 8 * rc;
+            if (inside) {
+                E *dst = D + (int64_t)(rbase + rr) * ldd + col;
+#pragma unroll
+                for (int q0 = 0; q0 < 16; q0 += 8) {  // LDS reads in batches of 8 ahead of the stores
+                    V8 v[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        v[q] = *reinterpret_cast<const V8 *>(piece(q0 + q) + rr * WTN +
+                                                             ((rc ^ ((4 * (q0 + q) + rr) & 15)) << 3));
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        *reinterpret_cast<V8 *>(dst + (int64_t)(4 * (q0 + q)) * ldd) = v[q];
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const V8 v = *reinterpret_cast<const V8 *>(piece(q) + rr * WTN + ((rc ^ ((4 * q + rr) & 15)) << 3));
+                    const int row = rbase + 4 * q + rr;
+                    if (row < M) {
+                        E *dst = D + (int64_t)row * ldd + col;
+                        if (dvec && col + 7 < N) {
+                            *reinterpret_cast<V8 *>(dst) = v;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                if (col + e < N)
+                                    dst[e] = v[e];
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    // prologue: K-tiles 0 and 1 of the first tile; wait for K-tile 0
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const auto ra = dma_rsrc(a_src, e, true), rb = dma_rsrc(b_src, e, true);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+            dma_a(ra, p);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+            dma_b(rb, p);
+        next_dma_stage();
+    }
+    wait_vmem<2 * PASSES>();
+    barrier_lds();
+#pragma unroll
+    for (int q = 0; q < NFRAG; ++q)
+        read_frag(0, 0, 0, q, fa[0], fb[0]);
+
+    int sa = 0, sb = 0;  // stages of the K-tile being multiplied
+    // One K-tile: K-step 0 with the three-stage operand's refill (K-tile dk
+    // of the DMA stream's tile), the wait for the next K-tile and the
+    // barrier that drains this one's stages, K-step 1 with the other
+    // operand's refill (unless `hold`: the caller issues it after the
+    // epilogue) reading K-step 0 of the next K-tile (unless `last`).
+    auto k_tile = [&](int dk, bool live, bool hold, bool last) __attribute__((always_inline)) {
+        step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], X3, dma_rsrc(X3 == 1 ? a_src : b_src, dk, live),
+             rs0_t{});
+        wait_vmem<PASSES>();  // all but that refill: the next K-tile has landed (this wave's part)
+        barrier_lds();        // ... for every wave; this K-tile's stages are drained
+        const int sa1 = sa + 1 == SA ? 0 : sa + 1, sb1 = sb + 1 == SB ? 0 : sb + 1;
+        step(fa[1], fb[1], !last, sa1, sb1, 0, fa[0], fb[0], hold ? 0 : Y2,
+             dma_rsrc(Y2 == 1 ? a_src : b_src, dk, live), rs4_t{});
+        if (!hold)
+            next_dma_stage();
+        sa = sa1;
+        sb = sb1;
+    };
+    for (int ci = 0; ci < mine; ++ci) {
+        for (int kt = 0; kt + 2 < KT; ++kt)
+            k_tile(kt + 2, true, false, false);
+        // the last two K-tiles refill K-tiles 0 and 1 of the next tile
+        const bool more = ci + 1 < mine;
+        if (more)
+            set_dma_tile(ci + 1);
+        k_tile(0, more, false, false);
+        const int esa = sa, esb = sb;  // stages of the last K-tile: the staging memory
+        k_tile(1, more, true, !more);
+        epilogue(ci, esa, esb);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging reads are done
+        const auto r = dma_rsrc(Y2 == 1 ? a_src : b_src, 1, more);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            if (Y2 == 1)
+                dma_a(r, p);
+            else
+                dma_b(r, p);
+        }
+        next_dma_stage();
+    }
+    wait_vmem<0>();  // no DMA or store may be outstanding when the wave ends
+}
+
 // ------------------------------------------------------------------------
 // Block-scaled FP8 GEMM ("TIRx Layout API", section "Scale Factor 布局": a
 // block-scaled MMA reads, besides its operands, one 8-bit scale factor per
@@ -1736,6 +2060,7 @@ struct KernelChoice {
     const char *tile;  // "<BM>x<BN>_w<WM>x<WN>"
     int bm, bn, threads;
     int path;
+    bool persistent = false;  // grid: one workgroup per compute unit, not one per tile
 };
 
 // Compile-time tuning of the direct-to-LDS kernels: K-tile depth (BK), LDS
@@ -1774,6 +2099,23 @@ struct KernelChoice {
 #endif
 #ifndef TG_S_MF
 #define TG_S_MF 16
+#endif
+
+// Persistent 256×256 kernel: stages of A (3: A three, B two; 2: the
+// reverse), tile rows per group of the tile order, fragment-read spacing of
+// the K-step before the barrier, and the tiles per compute unit from which
+// it replaces the one-tile-per-workgroup launch (0: never).
+#ifndef TG_P_SA
+#define TG_P_SA 3
+#endif
+#ifndef TG_P_GM
+#define TG_P_GM 4
+#endif
+#ifndef TG_P_RS0
+#define TG_P_RS0 4
+#endif
+#ifndef TG_P_MIN_PER_CU
+#define TG_P_MIN_PER_CU 2
 #endif
 
 // MFMA shape of the 256×256 kernel: 16 (v_mfma_f32_16x16x32, the default:
@@ -1845,6 +2187,7 @@ constexpr const char *TILE_STRIP64 = TG_TILE(64, TG_K_BN, 1, TG_K_WN);
 constexpr const char *TILE_STRIP128 = TG_TILE(128, 128, 2, 2) "_strip";
 constexpr const char *TILE_STRIP256 = TG_TILE(256, 128, 2, 2);
 constexpr const char *TILE_256 = TG_TILE(256, 256, 2, 2);
+constexpr const char *TILE_256P = TG_TILE(256, 256, 2, 2) "_pers";
 constexpr const char *TILE_128 = TG_TILE(128, 128, 2, 2);
 constexpr const char *TILE_64 = TG_TILE(64, 64, 2, 2);
 
@@ -1901,7 +2244,12 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     // smaller tile is 5–9% faster
     if (tiles(256, 256) >= 5 * NUM_CU / 8) {
         const LoadPath lp = path(256, 256);
-        if (lp == PATH_DMA)
+        // several tiles per compute unit and whole K-tiles: the persistent form
+        if (lp == PATH_DMA && TG_P_MIN_PER_CU > 0 && tiles(256, 256) >= TG_P_MIN_PER_CU * NUM_CU &&
+            K >= 128 && K % 64 == 0) {
+            k = {reinterpret_cast<const void *>(&gemm_pers_kernel<E, TG_P_SA, TG_P_GM, TG_P_RS0>), TILE_256P,
+                 256, 256, 256, PATH_DMA, true};
+        } else if (lp == PATH_DMA)
             k = {reinterpret_cast<const void *>(&gemm_dma3_kernel<E, 256, 256, 2, 2, TG_L_MF>), TILE_256, 256,
                  256, 256, PATH_DMA};
         else
@@ -1929,6 +2277,28 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
 
 // per-device "is gfx950" cache: 0 unknown, 1 yes, -1 no
 std::atomic<int> g_arch_ok[64];
+// per-device compute-unit count (0: not yet queried)
+std::atomic<int> g_cus[64];
+
+// Workgroups of a persistent launch: one per compute unit, rounded down to a
+// multiple of the 8 XCDs (workgroup w runs on XCD w mod 8, and the tile order
+// keeps each XCD's tiles together), never more than there are tiles.
+int64_t persistent_grid(int64_t tiles)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64)
+        cus = g_cus[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = NUM_CU;
+        if (dev >= 0 && dev < 64)
+            g_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    int64_t g = (int64_t)cus / NUM_XCD * NUM_XCD;
+    if (g < NUM_XCD)
+        g = NUM_XCD;
+    return g < tiles ? g : tiles;
+}
 
 int check_device()
 {
@@ -1962,9 +2332,10 @@ int launch(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t 
     if (st != TG_OK)
         return st;
     Plan p = make_plan<E>(A, B, D, M, N, K, lda, ldb, ldd);
-    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
-    if (grid >= LIMIT32)
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles >= LIMIT32)
         return TG_ERR_TOO_LARGE;
+    const int64_t grid = p.k.persistent ? persistent_grid(tiles) : tiles;
     int Mi = (int)M, Ni = (int)N, Ki = (int)K;
     void *args[] = {(void *)&A, (void *)&B, (void *)&D, &Mi, &Ni, &Ki, &lda, &ldb, &ldd,
                     &p.tiles_m, &p.tiles_n, &p.dvec};

@@ -35,9 +35,9 @@ extern "C" {
  *               for its distribution, or zeros for the unthrottled rate.
  *   waves_per_simd  1 (one workgroup of four waves per compute unit).
  *   iters       loop iterations; each wave issues 64 MFMAs of 16x16x32 (or
- *               16 of 32x32x16) per iteration on 256 independent fp32
- *               accumulators held in registers: 2^20 flop per wave per
- *               iteration either way.
+ *               32 of 32x32x16, two passes over 16 accumulators) per
+ *               iteration on 256 fp32 accumulators held in registers:
+ *               2^20 flop per wave per iteration either way.
  *   workgroups  workgroups of four waves (normally the compute-unit count).
  *   out         device pointer to workgroups·256 floats: each lane writes
  *               the sum of its accumulators (keeps the work observable).

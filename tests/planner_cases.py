@@ -57,6 +57,10 @@ _F16_BF16 = {
     ("256x256_w2x2", "dma"): Case(4100, 4200, 200),
     ("256x256_w2x2", "vec"): Case(257, 40960, 64, lda=vec_lda(256)),
     ("256x256_w2x2", "scalar"): Case(4100, 4200, 250),
+    # persistent 256x256 (at least 2 tiles per compute unit, K a multiple of
+    # 64 from 128): 561 tiles, so each of the 256 workgroups crosses 1-2 tile
+    # boundaries inside its K-tile stream; ragged M and N
+    ("256x256_w2x2_pers", "dma"): Case(4100, 8200, 192),
     ("128x128_w2x2", "dma"): Case(2100, 2000, 200),
     ("128x128_w2x2", "vec"): Case(129, 5120, 64, lda=vec_lda(128)),
     ("128x128_w2x2", "scalar"): Case(1000, 2000, 250),
@@ -81,8 +85,10 @@ MX_CASES: dict[str, Case] = {
 
 TILES = sorted({t for t, _ in _F16_BF16})
 PATHS = ("dma", "vec", "scalar")
+DMA_ONLY = {"256x256_w2x2_pers"}  # tiles whose kernels exist only on the direct-to-LDS path
 
 
 def all_fp_names() -> set:
     """Every name the fp16/bf16 planners can return."""
-    return {f"gemm_{dt}_{t}_{p}" for dt in ("f16", "bf16") for t in TILES for p in PATHS}
+    return {f"gemm_{dt}_{t}_{p}" for dt in ("f16", "bf16") for t in TILES for p in PATHS
+            if p == "dma" or t not in DMA_ONLY}

@@ -368,3 +368,46 @@ def test_torch_wrapper_refuses_overlapping_rows_and_mixed_devices():
     torch.cuda.synchronize()
     res = oracle.gemm(x.cpu().numpy(), B.cpu().numpy(), 1, 32, 64)
     _check(D.cpu().numpy(), res, "one-row wrapper")
+
+
+@pytest.mark.parametrize("K", [128, 192, 320])
+def test_persistent_crosses_tile_boundaries_exact(K):
+    """The persistent 256x256 kernel on 17 x 33 = 561 tiles: each of its 256
+    workgroups takes two or three tiles, so its K-tile stream crosses tile
+    boundaries (the next tile's first K-tiles load during the previous
+    tile's last two; the epilogue is staged in the drained stages).  K spans
+    2, 3 and 5 K-tiles; ragged M and N; D inside a guard band with an odd
+    row stride (element-wise epilogue stores).  Integer operands: D must
+    equal the oracle bit for bit, and nothing outside D's window changes."""
+    M, N = 4100, 8200
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N + 6)
+    assert st0 == tg.TG_OK and name == "gemm_f16_256x256_w2x2_pers_dma" and tiles == 561
+    a, b = workloads.index_pattern(M, N, K)
+    d, full, st = run(a, b, M, N, K, guard=3, label=f"persistent exact K={K}")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 3)
+    res = oracle.gemm(a, b, M, N, K)
+    assert np.array_equal(_bits(d), _bits(res.d))
+
+
+def test_persistent_random_data_sampled():
+    """Random N(0,1) and N(0,1/K) operands through the persistent kernel at a
+    shape with a partial last wave (2 or 3 tiles per workgroup) and full
+    K = 4096: sampled rows and every row of the last tile row, checked
+    against the oracle's tolerance."""
+    M, N, K = 4096 + 200, 8192 + 56, 4096
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N)
+    assert name == "gemm_f16_256x256_w2x2_pers_dma" and tiles == 17 * 33
+    a = workloads.random_f16(5101, (M, K))
+    b = workloads.random_f16(5102, (N, K), ("normal", 0.0, 1.0 / 64))
+    say("persistent random: upload")
+    A = torch.from_numpy(a).to("cuda:0")
+    B = torch.from_numpy(b).to("cuda:0")
+    D = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    st = tg.tg_gemm_f16(A, B, D, M, N, K, K, K, N, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == tg.TG_OK
+    rows = np.unique(np.concatenate([workloads.sample_rows(workloads.Workload(9, "t", M, N, K, (), ()), 48),
+                                     np.arange(4096, M)]))
+    res = oracle.gemm(a, b, M, N, K, rows=rows)
+    _check(D[torch.from_numpy(rows).to("cuda:0")].cpu().numpy(), res, "persistent random")
+    assert bool(torch.isfinite(D).all())

@@ -46,7 +46,7 @@ def test_planner_sweep_stays_inside_the_table():
     Ns = [131, 300, 2000, 5120, 16256, 16385, 16411, 40960]
     seen = set()
     for fmt, M, N in itertools.product(("f16", "bf16"), Ms, Ns):
-        for K, a_off in ((64, 0), (200, 0), (250, 0), (96, 1)):
+        for K, a_off in ((64, 0), (128, 0), (200, 0), (250, 0), (96, 1)):
             for lda in (K, vec_lda(256), vec_lda(128), vec_lda(64)):
                 name = _plan(fmt, M, N, K, lda, K, a_off)
                 assert name in CASES, (fmt, M, N, K, lda, a_off, name)
@@ -64,3 +64,20 @@ def test_mx_planner_sweep_stays_inside_the_table():
         assert st == tg.TG_OK and name in MX_CASES, (M, N, K, name)
         seen.add(name)
     assert seen == set(MX_CASES)
+
+
+def test_persistent_kernel_conditions():
+    """The persistent 256x256 kernel takes direct-to-LDS launches with at
+    least two tiles per compute unit (512 tiles on 256 units) and K a
+    multiple of 64 from 128; everything else stays on the one-tile-per-
+    workgroup kernels."""
+    pers, one = "gemm_f16_256x256_w2x2_pers_dma", "gemm_f16_256x256_w2x2_dma"
+    assert _plan("f16", 8192, 14336, 4096, 4096, 4096) == pers   # the linear-layer shape: 1792 tiles
+    assert _plan("f16", 4096, 4096, 4096, 4096, 4096) == one     # 256 tiles: one per unit
+    assert _plan("f16", 4096, 8192, 4096, 4096, 4096) == pers    # 16 x 32 = 512 tiles
+    assert _plan("f16", 4096, 7936, 4096, 4096, 4096) == one     # 16 x 31 = 496 tiles
+    assert _plan("f16", 8192, 14336, 128, 128, 128) == pers      # two K-tiles
+    assert _plan("f16", 8192, 14336, 64, 64, 64) == one          # one K-tile
+    assert _plan("f16", 8192, 14336, 4160, 4160, 4160) == pers
+    assert _plan("f16", 8192, 14336, 4104, 4104, 4104) == one    # a partial K-tile
+    assert _plan("bf16", 8192, 14336, 4096, 4096, 4096) == "gemm_bf16_256x256_w2x2_pers_dma"
