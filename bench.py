@@ -398,6 +398,45 @@ def mfma_ceiling(w, args) -> int:
     return 0
 
 
+def hbm_ceiling(args, nbytes: int = 1 << 30) -> int:
+    """Time tg_hbm_read_ceiling (every byte of a buffer read once with
+    16-byte loads) with the GEMM's protocol, alternating two 1 GiB buffers so
+    the last-level cache (256 MB) cannot serve a call from the previous one;
+    for several workgroup counts.  Prints one JSON line with GB/s each."""
+    import torch
+
+    import dense_fp16_gemm_02_amd as tg
+
+    dev = torch.device("cuda:0")
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(i + 1) for i in range(2)]
+    st, cus, clk_khz, arch = tg.tg_device_info()
+    if st != tg.TG_OK:
+        raise RuntimeError(tg.tg_status_string(st))
+    stream = torch.cuda.current_stream(dev)
+    results = {}
+    for per_cu in (4, 8, 16):
+        wg = cus * per_cu
+        out = torch.empty(wg * 256, dtype=torch.int32, device=dev)
+
+        def step(i, wg=wg, out=out):
+            s = tg.tg_hbm_read_ceiling(bufs[i % 2], nbytes, wg, out, stream)
+            if s != tg.TG_OK:
+                raise RuntimeError(f"tg_hbm_read_ceiling: {tg.tg_status_string(s)}")
+
+        t = _timed(step, args.steps, args.warmup, max(1, args.records), args.per_call, dev, stream)
+        gbs = nbytes / (t["ms"] * 1e-3) / 1e9
+        results[f"read_{per_cu}wg_per_cu"] = {"ms_per_launch": round(t["ms"], 6), "gbs": round(gbs, 1),
+                                               "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"streaming read, {wg} workgroups: {t['ms'] * 1e3:9.2f} us per GiB  {gbs:8.1f} GB/s "
+            f"({100 * gbs / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f})")
+    line = {"metric": "GB/s of a streaming HBM read (tg_hbm_read_ceiling)", "unit": "GB/s", "bytes": nbytes,
+            "steps": args.steps, "warmup": args.warmup, "peak": PEAK_HBM_GBS,
+            "device": {"arch": arch, "compute_units": cus, "max_sclk_mhz": clk_khz / 1000},
+            "results": results}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def algorithmic_bytes(w, dtype: str) -> int:
     """Compulsory HBM bytes of one call: A and B read once, D (fp16) written once;
     the block-scaled entry point reads 1-byte codes plus one scale byte per 32 K
@@ -426,6 +465,9 @@ def main() -> int:
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only time the matrix-core stream (tg_mfma_ceiling) on the workload's A and B "
                          "and on zeros, for both MFMA shapes; one JSON line")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="only time a streaming read of HBM (tg_hbm_read_ceiling) over two alternating "
+                         "1 GiB buffers; one JSON line")
     ap.add_argument("--ceiling-iters", type=int, default=1024,
                     help="loop iterations per ceiling launch (2^20 flop per wave each)")
     ap.add_argument("--all", action="store_true",
@@ -479,6 +521,8 @@ def main() -> int:
 
     if args.mfma_ceiling:
         return mfma_ceiling(w, args)
+    if args.hbm_ceiling:
+        return hbm_ceiling(args)
 
     if args.all:
         pk = PEAK_FP8_TFLOPS if args.dtype == "mxf8" else PEAK_FP16_TFLOPS

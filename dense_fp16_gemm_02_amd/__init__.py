@@ -23,7 +23,7 @@ import os
 __all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_ERR_TOO_LARGE",
            "TG_ERR_LAYOUT", "tg_gemm_mxf8", "tg_gemm_mxf8_plan",
            "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_gemm_bf16",
-           "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "tg_mfma_ceiling", "gemm"]
+           "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "tg_mfma_ceiling", "tg_hbm_read_ceiling", "gemm"]
 
 TG_OK = 0
 TG_ERR_INVALID_ARG = -1
@@ -75,6 +75,8 @@ def load():
     lib.tg_mfma_ceiling.restype = ctypes.c_int
     lib.tg_mfma_ceiling.argtypes = [ctypes.c_int, vp, i64, vp, i64, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, vp, vp]
+    lib.tg_hbm_read_ceiling.restype = ctypes.c_int
+    lib.tg_hbm_read_ceiling.argtypes = [vp, i64, ctypes.c_int, vp, vp]
     lib.tg_device_info.restype = ctypes.c_int
     lib.tg_device_info.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                    ctypes.c_char_p, i64]
@@ -151,6 +153,12 @@ def tg_mfma_ceiling(shape: int, A, a_elems: int, B, b_elems: int, waves_per_simd
     include/tg_ceiling.h); returns the C status code."""
     return load().tg_mfma_ceiling(shape, _ptr(A), a_elems, _ptr(B), b_elems, waves_per_simd, iters,
                                   workgroups, _ptr(out), _stream(stream))
+
+
+def tg_hbm_read_ceiling(src, nbytes: int, workgroups: int, out, stream=None) -> int:
+    """Enqueue one streaming read of nbytes at src (measurement only; see
+    include/tg_ceiling.h); returns the C status code."""
+    return load().tg_hbm_read_ceiling(_ptr(src), nbytes, workgroups, _ptr(out), _stream(stream))
 
 
 def tg_status_string(status: int) -> str:

@@ -1,6 +1,8 @@
-// tg_ceiling.hip — a stream of independent matrix-core operations with no
-// memory traffic, for measuring what the matrix cores sustain on their own
-// under the part's power limit (declared in include/tg_ceiling.h).
+// tg_ceiling.hip — the two rates the GEMM kernels are held against, measured
+// on the part itself (declared in include/tg_ceiling.h): a stream of
+// independent matrix-core operations with no memory traffic (what the
+// matrix cores sustain under the power limit), and a streaming read of HBM
+// (what a read-bound kernel can reach).
 //
 // One workgroup of four waves per compute unit, one wave per SIMD.  Each
 // wave loads 16 operand registers of 8 binary16 values (8 "A" and 8 "B"
@@ -99,7 +101,46 @@ __global__ __launch_bounds__(256) void mfma_stream_kernel(const _Float16 *__rest
     out[w * 64 + lane_end] = s;
 }
 
+// Streaming read of a buffer: 16 bytes per lane per load, four loads in
+// flight per lane, grid-stride over the whole buffer; each lane folds what
+// it read into one word (so no load is dead) and writes it out at the end.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4 *__restrict__ p, int64_t n16,
+                                                       unsigned *__restrict__ out)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    unsigned acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(p + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace
+
+extern "C" int tg_hbm_read_ceiling(const void *src, int64_t bytes, int workgroups, unsigned *out, void *stream)
+{
+    if (!src || !out || bytes < 16 || bytes % 16 || workgroups < 1 || (uintptr_t)src % 16)
+        return TG_ERR_INVALID_ARG;
+    const u32x4 *p = static_cast<const u32x4 *>(src);
+    int64_t n16 = bytes / 16;
+    void *args[] = {(void *)&p, &n16, (void *)&out};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&hbm_read_kernel), dim3((unsigned)workgroups),
+                                   dim3(256), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
 
 extern "C" int tg_mfma_ceiling(int shape, const void *A, int64_t a_elems, const void *B, int64_t b_elems,
                                int waves_per_simd, int iters, int workgroups, float *out, void *stream)

@@ -1985,16 +1985,27 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
         const int nv = nblk - 4 * ktile(t);
         const uint32_t keep = nv >= 4 ? 0xffffffffu : (1u << (8 * nv)) - 1u;
         const uint32_t unit = 0x7f7f7f7fu & ~keep;
-        // word kt mod 4 of row r sits at byte 16·r + 4·(kt mod 4) of the slot
-        // (B's rows after A's 64)
-        const uint32_t *sw = reinterpret_cast<const uint32_t *>(sc_ring + slot(t) * SC_SLOT) + ktile(t) % 4;
+        // the four words of row r sit at bytes 16·r .. 16·r+15 of the slot
+        // (B's rows after A's 64); each lane reads its row's whole 16 bytes
+        // — sixteen consecutive rows fill all 64 banks once, where 4-byte
+        // reads 16 bytes apart put two rows on every bank — and keeps word
+        // kt mod 4 (a wave-uniform choice)
+        // (the empty asm keeps the compiler from narrowing the read back to
+        // the one word used)
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 *sw = reinterpret_cast<const u32x4 *>(sc_ring + slot(t) * SC_SLOT);
+        const int wsel = ktile(t) % 4;
+        auto pick = [wsel](u32x4 v) {
+            asm volatile("" : "+v"(v));
+            return wsel == 0 ? v[0] : wsel == 1 ? v[1] : wsel == 2 ? v[2] : v[3];
+        };
         uint32_t wa[TM], wb[TN];
 #pragma unroll
         for (int q = 0; q < TM; ++q)
-            wa[q] = ((sw[4 * (q * 32 + srow)] & keep) | unit) >> (8 * shalf);
+            wa[q] = ((pick(sw[q * 32 + srow]) & keep) | unit) >> (8 * shalf);
 #pragma unroll
         for (int q = 0; q < TN; ++q)
-            wb[q] = ((sw[4 * (64 + wave * WTN + q * 32 + srow)] & keep) | unit) >> (8 * shalf);
+            wb[q] = ((pick(sw[64 + wave * WTN + q * 32 + srow]) & keep) | unit) >> (8 * shalf);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             i32x8 fa[TM], fb[TN];

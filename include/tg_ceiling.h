@@ -1,6 +1,7 @@
 /*
- * tg_ceiling.h — measurement entry point of libtg_gemm.so: the rate the
- * matrix cores sustain on their own, with no memory traffic.
+ * tg_ceiling.h — measurement entry points of libtg_gemm.so: the rate the
+ * matrix cores sustain on their own, with no memory traffic, and the rate a
+ * streaming read of HBM reaches.
  *
  * The GEMM of tg_gemm.h is judged against the dense fp16 matrix-core peak.
  * That peak assumes the shader clock at its maximum; with random operands
@@ -50,6 +51,19 @@ extern "C" {
  */
 int tg_mfma_ceiling(int shape, const void *A, int64_t a_elems, const void *B, int64_t b_elems,
                     int waves_per_simd, int iters, int workgroups, float *out, void *stream);
+
+/*
+ * tg_hbm_read_ceiling — enqueue one streaming read of `bytes` bytes at src
+ * (device memory, 16-byte aligned, bytes a positive multiple of 16): every
+ * byte is loaded once with 16-byte non-temporal loads, four in flight per
+ * lane, by `workgroups` workgroups of 256 lanes striding over the buffer.
+ * The rate bytes / time is the practical HBM read bandwidth that the
+ * bandwidth-bound GEMM shapes (small M: B streamed once) are held against.
+ * out: device pointer to workgroups·256 unsigned words (each lane's XOR of
+ * what it read, so that no load is dead).  Returns TG_OK,
+ * TG_ERR_INVALID_ARG or TG_ERR_LAUNCH.  Asynchronous.
+ */
+int tg_hbm_read_ceiling(const void *src, int64_t bytes, int workgroups, unsigned *out, void *stream);
 
 #ifdef __cplusplus
 }
