@@ -830,6 +830,174 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(OCC *(WM * WN > 4 ? 
     store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
 }
 
+// Producer/consumer form of the 128×128 tile ("TIRx 与高性能GEMM (上)":
+// the closing summary names the producer/consumer split as the step after
+// the multi-stage pipeline — warp specialization).  Eight waves, two per
+// SIMD: waves 0..3 are consumers (a 2×2 grid of 64×64 blocks of D, 16×16×32
+// MFMAs on 64 accumulators each, fragment reads from LDS), waves 4..7 are
+// producers (every operand DMA of the tile, nothing else).  A DMA that
+// stalls at issue — the memory pipeline backed up behind L2 misses — then
+// stalls only its producer wave, while the consumer on the same SIMD keeps
+// issuing MFMAs.  On CDNA all waves of a workgroup get the same register
+// allocation, so the split fits where a consumer needs at most half the
+// register file: here, not at 256×256.
+//
+// STAGES LDS stages of 32 KiB (A's and B's 128 rows of one 64-K tile, the
+// same swizzle and source-side DMA addressing as the other kernels).  One
+// workgroup barrier per K-tile, in the middle of the consumers' K-tile t:
+// before it the producers wait until K-tile t+1 has landed and the
+// consumers finish reading stage t; after it the producers refill stage t
+// with K-tile t+STAGES.  A partial K-tile is the first one (its columns
+// below 0 read as zero); K-tiles past the end get empty ranges.  A last
+// barrier after the producers' final wait frees all stages for the
+// consumers' staged epilogue.
+template <typename E, int STAGES>
+__global__ __launch_bounds__(512) TG_WAVES_PER_SIMD(2) void gemm_ws_kernel(
+    const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
+    int dvec)
+{
+    using V8 = typename Elem<E>::v8;
+    using V4 = typename Elem<E>::v4;
+    constexpr int BM = 128, BN = 128, BK_ = 64, MF = 16;
+    using T = OperandTile<BK_>;
+    constexpr int NC = 4;                       // consumer waves (and producer waves)
+    constexpr int WTM = 64, WTN = 64;           // consumer block
+    constexpr int TM = WTM / MF, TN = WTN / MF;
+    constexpr int CPK = 4;
+    constexpr int PIECE = T::ROWS_PER_DMA * BK_;               // elements one DMA fills (1 KiB)
+    constexpr int PASSES = BM / T::ROWS_PER_DMA / NC;          // DMAs per producer per operand K-tile
+    constexpr int DPT = 2 * PASSES;                            // DMAs per producer per K-tile
+    constexpr int STAGE = (BM + BN) * BK_;
+    static_assert(STAGES >= 3 && STAGES * STAGE * 2 <= 160 * 1024, "LDS budget");
+    static_assert((STAGES - 1) * DPT <= 63, "vmcnt holds 6 bits");
+    static_assert(NC * WTM * WTN <= STAGE * STAGES, "staging fits");
+
+    __shared__ __attribute__((aligned(1024))) E smem[STAGES * STAGE];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int KT = (K + BK_ - 1) / BK_;
+    const int k0 = K - BK_ * KT;  // <= 0: the first K-tile may be partial
+
+    if (wave >= NC) {
+        // ---------------- producer: DMA pieces 4p + pw of A and of B
+        const int pw = wave - NC;
+        const int dr = lane / T::RC;
+        static_assert((NC * T::ROWS_PER_DMA) % 16 == 0, "swizzle repeats per pass");
+        const int kc = (lane % T::RC) ^ T::swz(T::ROWS_PER_DMA * pw + dr);
+        uint32_t a_off[PASSES], b_off[PASSES];
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int t = T::ROWS_PER_DMA * (p * NC + pw) + dr;
+            a_off[p] = (uint32_t)(imin(t, M - 1 - m0) * lda * 2 + 16 * kc);
+            b_off[p] = (uint32_t)(imin(t, N - 1 - n0) * ldb * 2 + 16 * kc);
+        }
+        const char *a_tile = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
+        const char *b_tile = reinterpret_cast<const char *>(B + (int64_t)n0 * ldb);
+        auto issue = [&](int t, bool first) {
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a_tile + 2 * (int64_t)(k0 + t * BK_)), (short)0, t < KT ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
+            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(b_tile + 2 * (int64_t)(k0 + t * BK_)), (short)0, t < KT ? DMA_RANGE : 0, BUFFER_RSRC_WORD3);
+            E *st = smem + (t % STAGES) * STAGE;
+            const bool neg = first && k0 + 8 * kc < 0;  // columns below 0 of the partial first K-tile
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p)
+                dma16<CPOL_CACHED>(ra, st + (p * NC + pw) * PIECE, neg ? DMA_OOB : a_off[p]);
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p)
+                dma16<CPOL_CACHED>(rb, st + BM * BK_ + (p * NC + pw) * PIECE, neg ? DMA_OOB : b_off[p]);
+        };
+        issue(0, true);
+#pragma unroll
+        for (int t = 1; t < STAGES; ++t)
+            issue(t, false);
+        wait_vmem<(STAGES - 1) * DPT>();  // K-tile 0 has landed
+        barrier_lds();  // (not __syncthreads: that would wait for every DMA in flight)
+        for (int t = 0; t < KT; ++t) {
+            wait_vmem<(STAGES - 2) * DPT>();  // K-tile t+1 has landed
+            barrier_lds();                   // consumers are done with stage t
+            issue(t + STAGES, false);
+        }
+        wait_vmem<0>();
+        barrier_lds();  // every stage is free for the epilogue
+        return;
+    }
+
+    // ---------------- consumer
+    const int wm = wave / 2, wn = wave % 2;
+    const int frag_row = frag16_row_of(lane), frag_hi = frag16_hi_of(lane);
+    int a_lane[2], b_lane[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        a_lane[kk] = T::off(wm * WTM + frag_row, kk * CPK + frag_hi);
+        b_lane[kk] = BM * BK_ + T::off(wn * WTN + frag_row, kk * CPK + frag_hi);
+    }
+    static_assert(T::swz(16) == T::swz(0), "swizzle period");
+    V8 fa[2][TM], fb[2][TN];
+    auto read_frag = [&](int s, int kk, int q, V8 *a, V8 *b) {
+        const E *st = smem + s * STAGE;
+        if (q < TM)
+            a[q] = *reinterpret_cast<const V8 *>(st + a_lane[kk] + q * MF * BK_);
+        else
+            b[q - TM] = *reinterpret_cast<const V8 *>(st + b_lane[kk] + (q - TM) * MF * BK_);
+    };
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int NFRAG = TM + TN, SLOTS = TM * TN, RS = SLOTS / NFRAG;
+    static_assert(RS >= 1, "reads fit the slots");
+    auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
+    auto step = [&](const V8 *a, const V8 *b, int rs, int rkk, V8 *na, V8 *nb) {
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            acc[i / TN][i % TN] = Elem<E>::mfma(b[i % TN], a[i / TN], acc[i / TN][i % TN]);
+            MFMA_FIRST();
+            if (i % RS == 0 && i / RS < NFRAG)
+                read_frag(rs, rkk, frag_of_slot(i / RS), na, nb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    barrier_lds();  // K-tile 0 has landed
+#pragma unroll
+    for (int q = 0; q < NFRAG; ++q)
+        read_frag(0, 0, q, fa[0], fb[0]);
+    int s = 0;
+    for (int t = 0; t < KT; ++t) {
+        step(fa[0], fb[0], s, 1, fa[1], fb[1]);
+        barrier_lds();  // this K-tile's stage is read; K-tile t+1 has landed
+        const int s1 = s + 1 == STAGES ? 0 : s + 1;
+        step(fa[1], fb[1], s1, 0, fa[0], fb[0]);  // (past the last K-tile the reads are unused)
+        s = s1;
+    }
+    barrier_lds();  // the producers' last DMAs have landed: every stage is free
+
+    // staged epilogue: each consumer stages its 64×64 block in its own 8 KiB
+    constexpr int SROW = WTN, SCH = WTN / 8;
+    auto stage_off = [](int r, int chunk) { return r * SROW + ((chunk ^ (r & (SCH - 1))) << 3); };
+    E *stg = smem + wave * WTM * WTN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            V4 h;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                h[r] = (E)acc[i][j][r];  // round to nearest even
+            const int r = i * MF + frag_row;
+            const int c = j * MF + frag_hi * 4;
+            *reinterpret_cast<V4 *>(stg + stage_off(r, c / 8) + (c & 7)) = h;
+        }
+    store_staged_block<E, WTM, WTN>(stg, stage_off, D, ldd, m0 + wm * WTM, n0 + wn * WTN, M, N, dvec, lane);
+}
+
 // Variant of gemm_dma_kernel for the largest tile with separate LDS rings
 // for the two operands: three stages of A and two of B (BK = 64: 3·32 + 2·32
 // KiB = 160 KiB for 256×256).  With one ring of two stages the refill of a
@@ -2105,6 +2273,17 @@ struct KernelChoice {
 // MFMA shape per tile (16: v_mfma_f32_16x16x32, 32: v_mfma_f32_32x32x16).
 // The 64×64 tile runs faster with the 16×16 shape (10–15% on 1000³, 1024³,
 // 512×512×4096); the 128×128 tile measured mixed (−5% to +2%), so keeps 32.
+// Producer/consumer 128×128 kernel in place of the 128×128 one on the
+// direct-to-LDS path (1) or not (0), and its LDS stages.  Measured on one
+// box (steady state): 2048×2048×4096 43.2 → 34.4 µs, 2048×4096×4096 81.5 →
+// 65.4, 1536×3072×4096 63.1 → 53.7, 2560³ 48.6 → 41.6, 3072²×1024 32.9 →
+// 29.5, 2048³ 22.1 → 20.9; three, four or five stages within 2%.
+#ifndef TG_WS_ON
+#define TG_WS_ON 1
+#endif
+#ifndef TG_WS_STAGES
+#define TG_WS_STAGES 4
+#endif
 #ifndef TG_M_MF
 #define TG_M_MF 32
 #endif
@@ -2127,6 +2306,12 @@ struct KernelChoice {
 #endif
 #ifndef TG_P_MIN_PER_CU
 #define TG_P_MIN_PER_CU 2
+#endif
+
+// Tiles of 256×256 from which that tile replaces the 128×128 one (5/8 of
+// the compute units).
+#ifndef TG_L_MIN_TILES
+#define TG_L_MIN_TILES (5 * NUM_CU / 8)
 #endif
 
 // MFMA shape of the 256×256 kernel: 16 (v_mfma_f32_16x16x32, the default:
@@ -2200,6 +2385,7 @@ constexpr const char *TILE_STRIP256 = TG_TILE(256, 128, 2, 2);
 constexpr const char *TILE_256 = TG_TILE(256, 256, 2, 2);
 constexpr const char *TILE_256P = TG_TILE(256, 256, 2, 2) "_pers";
 constexpr const char *TILE_128 = TG_TILE(128, 128, 2, 2);
+constexpr const char *TILE_128WS = TG_TILE(128, 128, 2, 2) "_ws";
 constexpr const char *TILE_64 = TG_TILE(64, 64, 2, 2);
 
 constexpr int64_t LIMIT32 = (int64_t)1 << 31;
@@ -2253,7 +2439,7 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     // the 128×128 tiles by 20–40% at 160–224 tiles (the 128×128 grid then
     // runs 2.5–3.5 waves); at 128 tiles (exactly two waves of 128×128) the
     // smaller tile is 5–9% faster
-    if (tiles(256, 256) >= 5 * NUM_CU / 8) {
+    if (tiles(256, 256) >= TG_L_MIN_TILES) {
         const LoadPath lp = path(256, 256);
         // several tiles per compute unit and whole K-tiles: the persistent form
         if (lp == PATH_DMA && TG_P_MIN_PER_CU > 0 && tiles(256, 256) >= TG_P_MIN_PER_CU * NUM_CU &&
@@ -2270,9 +2456,15 @@ Plan make_plan(const void *A, const void *B, const void *D, int64_t M, int64_t N
     // grid by 15–90% (1152²×1024, 1024×1536×4096, 2048×1280×4096,
     // 1792×2048×2048); at 48–64 (1000³, 1024²×4096, 768×1024×4096) the
     // 64×64 grid is faster
-    else if (tiles(128, 128) >= 5 * NUM_CU / 16)
-        k = choice<E, 128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT, TG_M_MF>(
-            path(128, 128), TILE_128);
+    else if (tiles(128, 128) >= 5 * NUM_CU / 16) {
+        const LoadPath lp = path(128, 128);
+        if (lp == PATH_DMA && TG_WS_ON)
+            k = {reinterpret_cast<const void *>(&gemm_ws_kernel<E, TG_WS_STAGES>), TILE_128WS, 128, 128, 512,
+                 PATH_DMA};
+        else
+            k = choice<E, 128, 128, 2, 2, TG_M_BK, TG_M_STAGES, TG_M_DMA_STEPS, 1, TG_M_KROT, TG_M_MF>(
+                lp, TILE_128);
+    }
     else
         k = choice<E, 64, 64, 2, 2, TG_S_BK, TG_S_STAGES, TG_S_DMA_STEPS, 1, TG_S_KROT, TG_S_MF>(
             path(64, 64), TILE_64);

@@ -61,7 +61,8 @@ _F16_BF16 = {
     # 64 from 128): 561 tiles, so each of the 256 workgroups crosses 1-2 tile
     # boundaries inside its K-tile stream; ragged M and N
     ("256x256_w2x2_pers", "dma"): Case(4100, 8200, 192),
-    ("128x128_w2x2", "dma"): Case(2100, 2000, 200),
+    # 128x128 on the direct-to-LDS path: the producer/consumer kernel
+    ("128x128_w2x2_ws", "dma"): Case(2100, 2000, 200),
     ("128x128_w2x2", "vec"): Case(129, 5120, 64, lda=vec_lda(128)),
     ("128x128_w2x2", "scalar"): Case(1000, 2000, 250),
     ("64x64_w2x2", "dma"): Case(1000, 1000, 200),
@@ -85,10 +86,11 @@ MX_CASES: dict[str, Case] = {
 
 TILES = sorted({t for t, _ in _F16_BF16})
 PATHS = ("dma", "vec", "scalar")
-DMA_ONLY = {"256x256_w2x2_pers"}  # tiles whose kernels exist only on the direct-to-LDS path
+DMA_ONLY = {"256x256_w2x2_pers", "128x128_w2x2_ws"}  # kernels only on the direct-to-LDS path
+NO_DMA = {"128x128_w2x2"}  # kernels whose direct-to-LDS form is another kernel
 
 
 def all_fp_names() -> set:
     """Every name the fp16/bf16 planners can return."""
     return {f"gemm_{dt}_{t}_{p}" for dt in ("f16", "bf16") for t in TILES for p in PATHS
-            if p == "dma" or t not in DMA_ONLY}
+            if (p == "dma" or t not in DMA_ONLY) and not (p == "dma" and t in NO_DMA)}

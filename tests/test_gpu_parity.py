@@ -411,3 +411,42 @@ def test_persistent_random_data_sampled():
     res = oracle.gemm(a, b, M, N, K, rows=rows)
     _check(D[torch.from_numpy(rows).to("cuda:0")].cpu().numpy(), res, "persistent random")
     assert bool(torch.isfinite(D).all())
+
+
+@pytest.mark.parametrize("M,N,K", [(2100, 2000, 200), (2048, 4096, 328), (1537, 3001, 72), (3072, 3072, 64),
+                                   (2048, 2048, 8), (1300, 2700, 136)])
+def test_producer_consumer_tile_exact(M, N, K):
+    """The producer/consumer 128x128 kernel (four waves only issue DMAs, four
+    only multiply): K from 1 to 6 K-tiles with partial first K-tiles, ragged
+    M and N, D inside a guard band with an odd row stride.  Integer operands:
+    D equals the oracle bit for bit and nothing outside D's window changes."""
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N + 4)
+    assert st0 == tg.TG_OK and name == "gemm_f16_128x128_w2x2_ws_dma"
+    a, b = workloads.index_pattern(M, N, K)
+    d, full, st = run(a, b, M, N, K, guard=2, label=f"producer/consumer exact {M}x{N}x{K}")
+    assert st == tg.TG_OK and guard_intact(full, M, N, 2)
+    res = oracle.gemm(a, b, M, N, K)
+    assert np.array_equal(_bits(d), _bits(res.d))
+
+
+def test_producer_consumer_tile_random_data():
+    """Random N(0,1) and N(0,1/K) operands through the producer/consumer
+    128x128 kernel at K = 4096, checked on sampled rows and the last tile row
+    against the oracle's tolerance."""
+    M, N, K = 2048 + 100, 4096 - 24, 4096
+    st0, name, tiles = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N)
+    assert name == "gemm_f16_128x128_w2x2_ws_dma"
+    a = workloads.random_f16(5201, (M, K))
+    b = workloads.random_f16(5202, (N, K), ("normal", 0.0, 1.0 / 64))
+    say("producer/consumer random: upload")
+    A = torch.from_numpy(a).to("cuda:0")
+    B = torch.from_numpy(b).to("cuda:0")
+    D = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    st = tg.tg_gemm_f16(A, B, D, M, N, K, K, K, N, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == tg.TG_OK
+    rows = np.unique(np.concatenate([workloads.sample_rows(workloads.Workload(9, "t", M, N, K, (), ()), 48),
+                                     np.arange(2048, M)]))
+    res = oracle.gemm(a, b, M, N, K, rows=rows)
+    _check(D[torch.from_numpy(rows).to("cuda:0")].cpu().numpy(), res, "producer/consumer random")
+    assert bool(torch.isfinite(D).all())

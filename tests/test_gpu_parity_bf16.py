@@ -71,6 +71,7 @@ def test_workload_sampled_rows(idx):
     (4136, 4120, 8, "256x256"), (4136, 4120, 72, "256x256"),
     (64, 16411, 200, "64x128"), (100, 16390, 256, "128x128"), (200, 16500, 136, "256x128"),
     (4100, 8200, 128, "256x256_w2x2_pers"), (4100, 8200, 256, "256x256_w2x2_pers"),
+    (2048, 4096, 256, "128x128_w2x2_ws"), (1537, 3001, 72, "128x128_w2x2_ws"),
 ])
 def test_small_int_pattern_exact(M, N, K, tile):
     """Operands in {-1, 0, 1} with K <= 256: D is exact in bf16, so every
