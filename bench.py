@@ -352,10 +352,12 @@ def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16"):
 
 def mfma_ceiling(w, args) -> int:
     """Time tg_mfma_ceiling (a stream of independent MFMAs on register
-    operands, no memory traffic) with the same protocol as the GEMM: the
-    operand registers loaded from the workload's own A and B (its value
-    distribution), and from zeros (no toggling, so no power limit).  Prints
-    one JSON line with TFLOP/s per MFMA shape and operand set."""
+    operands, no memory traffic) with the same protocol as the GEMM, for
+    each instruction the GEMM kernels use: the operand registers loaded from
+    the workload's own A and B (its value distribution: fp16, the same draws
+    rounded to bf16, or their block-scaled e4m3 codes), and from zeros (no
+    toggling, so no power limit).  Prints one JSON line with TFLOP/s per
+    instruction and operand set."""
     import numpy as np
     import torch
 
@@ -363,35 +365,53 @@ def mfma_ceiling(w, args) -> int:
     import workloads
 
     dev = torch.device("cuda:0")
+
+    def upload(x):
+        return torch.from_numpy(np.ascontiguousarray(x).reshape(-1).view(np.uint8)).to(dev)
+
     a, b = workloads.make_inputs(w)
-    A = torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16).reshape(-1)
-    B = torch.from_numpy(b.view(np.int16)).to(dev).view(torch.float16).reshape(-1)
-    Z = torch.zeros(1 << 16, dtype=torch.float16, device=dev)
+    ops = {"f16": (upload(a), upload(b))}
+    del a, b
+    a, b = workloads.make_inputs(w, dtype="bf16")
+    ops["bf16"] = (upload(a), upload(b))
+    del a, b
+    qa, _, qb, _ = workloads.make_mx_inputs(w)
+    ops["e4m3"] = (upload(qa), upload(qb))
+    del qa, qb
+    Z = torch.zeros(1 << 17, dtype=torch.uint8, device=dev)
     st, cus, clk_khz, arch = tg.tg_device_info()
     if st != tg.TG_OK:
         raise RuntimeError(tg.tg_status_string(st))
     out = torch.empty(cus * 256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     iters = args.ceiling_iters
-    flop = cus * 4 * iters * float(1 << 20)
+    # (code, name, operand type, bytes per element, flop per wave-iteration, peak)
+    shapes = [(tg.TG_MFMA_F16_16X16X32, "mfma_16x16x32_f16", "f16", 2, 1 << 20, PEAK_FP16_TFLOPS),
+              (tg.TG_MFMA_F16_32X32X16, "mfma_32x32x16_f16", "f16", 2, 1 << 20, PEAK_FP16_TFLOPS),
+              (tg.TG_MFMA_BF16_16X16X32, "mfma_16x16x32_bf16", "bf16", 2, 1 << 20, PEAK_FP16_TFLOPS),
+              (tg.TG_MFMA_MXF8_32X32X64, "mfma_scale_32x32x64_e4m3", "e4m3", 1, 1 << 21, PEAK_FP8_TFLOPS)]
     results = {}
-    for shape in (16, 32):
-        for label, (x, y) in (("workload", (A, B)), ("zeros", (Z, Z))):
-            def step(i, x=x, y=y, shape=shape):
-                s = tg.tg_mfma_ceiling(shape, x, x.numel(), y, y.numel(), 1, iters, cus, out, stream)
+    for code, base, kind, esize, per_iter, peak in shapes:
+        if args.ceiling_shapes and base not in args.ceiling_shapes.split(","):
+            continue
+        flop = cus * 4 * iters * float(per_iter)
+        for label, (x, y) in (("workload", ops[kind]), ("zeros", (Z, Z))):
+            def step(i, x=x, y=y, code=code, esize=esize):
+                s = tg.tg_mfma_ceiling(code, x, x.numel() // esize, y, y.numel() // esize, 1, iters, cus, out,
+                                       stream)
                 if s != tg.TG_OK:
                     raise RuntimeError(f"tg_mfma_ceiling: {tg.tg_status_string(s)}")
 
             t = _timed(step, args.steps, args.warmup, max(1, args.records), args.per_call, dev, stream)
             tf = flop / (t["ms"] * 1e-3) / 1e12
-            name = f"mfma_{shape}x{shape}x{512 // shape}_f16_{label}"
-            results[name] = {"ms_per_launch": round(t["ms"], 6), "tflops": round(tf, 1),
-                             "frac_of_peak": round(tf / PEAK_FP16_TFLOPS, 4)}
-            log(f"{name:36s} {t['ms'] * 1e3:9.2f} us/launch {tf:8.1f} TFLOP/s "
-                f"({100 * tf / PEAK_FP16_TFLOPS:.1f}% of {PEAK_FP16_TFLOPS:.0f})")
+            name = f"{base}_{label}"
+            results[name] = {"ms_per_launch": round(t["ms"], 6), "tflops": round(tf, 1), "peak": peak,
+                             "frac_of_peak": round(tf / peak, 4)}
+            log(f"{name:40s} {t['ms'] * 1e3:9.2f} us/launch {tf:8.1f} TFLOP/s "
+                f"({100 * tf / peak:.1f}% of {peak:.0f})")
     line = {"metric": "TFLOP/s of a matrix-core stream with no memory traffic (tg_mfma_ceiling)",
             "unit": "TFLOP/s", "workload_operands": w.name, "workgroups": cus, "iters": iters,
-            "steps": args.steps, "warmup": args.warmup, "peak": PEAK_FP16_TFLOPS,
+            "steps": args.steps, "warmup": args.warmup,
             "device": {"arch": arch, "compute_units": cus, "max_sclk_mhz": clk_khz / 1000},
             "results": results}
     print(json.dumps(line), flush=True)
@@ -468,6 +488,9 @@ def main() -> int:
     ap.add_argument("--hbm-ceiling", action="store_true",
                     help="only time a streaming read of HBM (tg_hbm_read_ceiling) over two alternating "
                          "1 GiB buffers; one JSON line")
+    ap.add_argument("--ceiling-shapes", default="",
+                    help="with --mfma-ceiling: comma-separated subset of mfma_16x16x32_f16, "
+                         "mfma_32x32x16_f16, mfma_16x16x32_bf16, mfma_scale_32x32x64_e4m3 (default all)")
     ap.add_argument("--ceiling-iters", type=int, default=1024,
                     help="loop iterations per ceiling launch (2^20 flop per wave each)")
     ap.add_argument("--all", action="store_true",

@@ -21,7 +21,8 @@ import ctypes
 import os
 
 __all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_ERR_TOO_LARGE",
-           "TG_ERR_LAYOUT", "tg_gemm_mxf8", "tg_gemm_mxf8_plan",
+           "TG_ERR_LAYOUT", "TG_MFMA_F16_16X16X32", "TG_MFMA_F16_32X32X16", "TG_MFMA_BF16_16X16X32",
+           "TG_MFMA_MXF8_32X32X64", "tg_gemm_mxf8", "tg_gemm_mxf8_plan",
            "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_gemm_bf16",
            "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "tg_mfma_ceiling", "tg_hbm_read_ceiling", "gemm"]
 
@@ -31,6 +32,12 @@ TG_ERR_LAUNCH = -2
 TG_ERR_DEVICE = -3
 TG_ERR_TOO_LARGE = -4
 TG_ERR_LAYOUT = -5
+
+# instruction codes of tg_mfma_ceiling (include/tg_ceiling.h)
+TG_MFMA_F16_16X16X32 = 16
+TG_MFMA_F16_32X32X16 = 32
+TG_MFMA_BF16_16X16X32 = 17
+TG_MFMA_MXF8_32X32X64 = 64
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libtg_gemm.so")

@@ -3,8 +3,9 @@
  * matrix cores sustain on their own, with no memory traffic, and the rate a
  * streaming read of HBM reaches.
  *
- * The GEMM of tg_gemm.h is judged against the dense fp16 matrix-core peak.
- * That peak assumes the shader clock at its maximum; with random operands
+ * The GEMMs of tg_gemm.h are judged against the dense matrix-core peaks
+ * (fp16 and bf16 2.5 PFLOP/s, fp8 5 PFLOP/s).  Those peaks assume the
+ * shader clock at its maximum; with random operands
  * the power limit lowers the clock, and a kernel doing nothing but matrix
  * multiply-accumulates shows what the part delivers under that limit
  * ("TIRx 与高性能GEMM (上)" measures its kernels against the matrix unit's
@@ -22,32 +23,41 @@
 extern "C" {
 #endif
 
+/* The instruction a matrix-core stream issues (the `shape` argument). */
+#define TG_MFMA_F16_16X16X32 16   /* v_mfma_f32_16x16x32_f16: the fp16 256x256 kernels */
+#define TG_MFMA_F16_32X32X16 32   /* v_mfma_f32_32x32x16_f16: the other fp16 tiles */
+#define TG_MFMA_BF16_16X16X32 17  /* v_mfma_f32_16x16x32_bf16: the bf16 256x256 kernels */
+#define TG_MFMA_MXF8_32X32X64 64  /* v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 x e4m3: block-scaled FP8 */
+
 /*
  * tg_mfma_ceiling — enqueue one launch of the matrix-core stream.
  *
- *   shape       16: v_mfma_f32_16x16x32_f16, 32: v_mfma_f32_32x32x16_f16
- *               (the two shapes the GEMM kernels use).
- *   A, B        device pointers to binary16 data of a_elems and b_elems
- *               elements (each at least 8 and a multiple of 8, 16-byte
- *               aligned).  Every wave loads its operand registers once from
- *               them (wave w, register set i, lane l reads the 8 elements at
- *               ((w·16 + i)·64 + l)·8 mod a_elems, likewise for B), so the
- *               stream multiplies the caller's data: pass the GEMM's A and B
- *               for its distribution, or zeros for the unthrottled rate.
+ *   shape       one of the TG_MFMA_* codes above.
+ *   A, B        device pointers to a_elems and b_elems elements of the
+ *               instruction's input type (binary16, bfloat16 or e4m3 bytes),
+ *               16-byte aligned; each count a positive multiple of 8 (16-bit
+ *               types) or 32 (e4m3).  Every wave loads its operand registers
+ *               once from them: fragment i of wave w, lane l is 16-byte chunk
+ *               ((w·16 + i)·64 + l) of the buffer, modulo its chunk count
+ *               (chunks 2c and 2c + 1 for the 32-byte e4m3 fragment c).  So
+ *               the stream multiplies the caller's data: pass the GEMM's A and B
+ *               for its distribution, or zeros for the unthrottled rate.  The
+ *               block-scaled form runs with unit scales (E8M0 127).
  *   waves_per_simd  1 (one workgroup of four waves per compute unit).
- *   iters       loop iterations; each wave issues 64 MFMAs of 16x16x32 (or
- *               32 of 32x32x16, two passes over 16 accumulators) per
- *               iteration on 256 fp32 accumulators held in registers:
- *               2^20 flop per wave per iteration either way.
+ *   iters       loop iterations on 256 fp32 accumulators held in registers.
+ *               Per wave and iteration: 64 MFMAs of 16x16x32 or 32 of
+ *               32x32x16 (two passes over 16 accumulators), 2^20 flop; or 16
+ *               of the block-scaled 32x32x64, 2^21 flop.
  *   workgroups  workgroups of four waves (normally the compute-unit count).
  *   out         device pointer to workgroups·256 floats: each lane writes
  *               the sum of its accumulators (keeps the work observable).
  *   stream      hipStream_t (NULL: the null stream).
  *
- * Flop per launch: workgroups · 4 · iters · 2^20.  Returns TG_OK,
- * TG_ERR_INVALID_ARG (a bad shape, a NULL pointer, a_elems or b_elems below
- * 8 or not a multiple of 8, iters < 1, workgroups < 1, waves_per_simd != 1),
- * TG_ERR_DEVICE or TG_ERR_LAUNCH.  Asynchronous.
+ * Flop per launch: workgroups · 4 · iters · 2^20 (2^21 for the block-scaled
+ * form).  Returns TG_OK, TG_ERR_INVALID_ARG (an unknown shape, a NULL or
+ * misaligned pointer, an element count below or not a multiple of the
+ * fragment size, iters < 1, workgroups < 1, waves_per_simd != 1),
+ * TG_ERR_DEVICE (not gfx950) or TG_ERR_LAUNCH.  Asynchronous.
  */
 int tg_mfma_ceiling(int shape, const void *A, int64_t a_elems, const void *B, int64_t b_elems,
                     int waves_per_simd, int iters, int workgroups, float *out, void *stream);

@@ -199,3 +199,30 @@ def test_torch_wrapper_refuses_cpu_tensors():
         tg.gemm(A, A)
     with pytest.raises(TypeError):
         tg.gemm(A, A.float())
+
+
+def test_ceiling_codes_and_validation():
+    """The instruction codes of tg_mfma_ceiling agree with include/tg_ceiling.h,
+    and bad arguments of both measurement entry points are rejected before a
+    device is touched."""
+    text = open(os.path.join(INCLUDE, "tg_ceiling.h")).read()
+    codes = dict(re.findall(r"#define (TG_MFMA_\w+) (\d+)", text))
+    assert len(codes) == 4
+    for name, value in codes.items():
+        assert getattr(tg, name) == int(value), name
+    ok = dict(A=FAKE, a=1 << 16, B=FAKE, b=1 << 16, w=1, it=4, wg=256, out=FAKE)
+    bad = [dict(shape=99), dict(shape=0),
+           dict(shape=tg.TG_MFMA_F16_16X16X32, a=12), dict(shape=tg.TG_MFMA_BF16_16X16X32, b=4),
+           dict(shape=tg.TG_MFMA_MXF8_32X32X64, a=48), dict(shape=tg.TG_MFMA_MXF8_32X32X64, b=16),
+           dict(shape=tg.TG_MFMA_F16_32X32X16, A=FAKE + 8), dict(shape=tg.TG_MFMA_MXF8_32X32X64, B=FAKE + 4),
+           dict(shape=tg.TG_MFMA_F16_16X16X32, A=None), dict(shape=tg.TG_MFMA_F16_16X16X32, out=None),
+           dict(shape=tg.TG_MFMA_F16_16X16X32, w=2), dict(shape=tg.TG_MFMA_F16_16X16X32, it=0),
+           dict(shape=tg.TG_MFMA_MXF8_32X32X64, wg=0)]
+    for kw in bad:
+        p = {**ok, **kw}
+        st = tg.tg_mfma_ceiling(p["shape"], p["A"], p["a"], p["B"], p["b"], p["w"], p["it"], p["wg"], p["out"])
+        assert st == tg.TG_ERR_INVALID_ARG, kw
+    for src, nbytes, wg, out in [(None, 1 << 20, 256, FAKE), (FAKE, 8, 256, FAKE), (FAKE, 1000, 256, FAKE),
+                                 (FAKE + 4, 1 << 20, 256, FAKE), (FAKE, 1 << 20, 0, FAKE),
+                                 (FAKE, 1 << 20, 256, None)]:
+        assert tg.tg_hbm_read_ceiling(src, nbytes, wg, out) == tg.TG_ERR_INVALID_ARG
