@@ -1641,9 +1641,11 @@ __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
 // 128×128, 128-byte operand rows in LDS (128 K per stage, two 64-K MFMA
 // K-steps per stage) with the same swizzle and source-side DMA addressing,
 // three A stages and two B stages.  Per iteration t:
-//   K-step 0: A(t+2) is DMAed;
+//   K-step 0: A(t+2) is DMAed while both halves of K-step 1's fragments
+//             are read (in the step's first half);
 //   wait until all but A(t+2) has landed; barrier; (at the first K-tile of
-//   a group) the scale words of the next group are loaded;
+//   a group, and the second in groups of four) the scale words of the next
+//   group are loaded;
 //   K-step 1: B(t+2) is DMAed while the fragments of K-tile t+1's K-step 0
 //             are read.
 // A scale word holds the four blocks of one row in one K-tile; lane r + 32·h
@@ -1804,13 +1806,16 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     const uint32_t sb_poff = (uint32_t)((wn * WTN + (lane >> 5) * 32 + srow) * ldsb);
     using GroupWord = typename MxGroup<MX_GROUP>::type;
     GroupWord gw[2][NPA + NPB] = {};  // [current, next group][pair]
-    auto load_group = [&](int t0, GroupWord *g) {
+    // Pairs [lo, hi) of the group starting at K-tile t0 (A pairs first).
+    auto load_group = [&](int t0, GroupWord *g, int lo, int hi) {
 #pragma unroll
         for (int p = 0; p < NPA; ++p)
-            g[p] = MxGroup<MX_GROUP>::load(sa_rsrc, (int)(sa_poff + 2 * p * sa_step + 4 * t0));
+            if (p >= lo && p < hi)
+                g[p] = MxGroup<MX_GROUP>::load(sa_rsrc, (int)(sa_poff + 2 * p * sa_step + 4 * t0));
 #pragma unroll
         for (int p = 0; p < NPB; ++p)
-            g[NPA + p] = MxGroup<MX_GROUP>::load(sb_rsrc, (int)(sb_poff + 2 * p * sb_step + 4 * t0));
+            if (NPA + p >= lo && NPA + p < hi)
+                g[NPA + p] = MxGroup<MX_GROUP>::load(sb_rsrc, (int)(sb_poff + 2 * p * sb_step + 4 * t0));
     };
     // Words of K-tile t (index j of group g) into sw_a[0] / sw_b[0], ready
     // for the MFMA: blocks at or past K/32 (the tail of a partial last
@@ -1864,8 +1869,12 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
                 acc[i][j][v] = 0.0f;
 
     auto frag_of_slot = [](int i) { return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN; };
-    // One K-step of K-tile t: MFMA per slot; after MFMA i, half i%2 of the
-    // next step's fragment i/2; DMA passes [0, n) of `o` in the odd slots.
+    // One K-step of K-tile t: MFMA per slot; DMA passes [0, n) of `o` in the
+    // odd slots.  The next step's fragments: in K-step 0 (whose reads must
+    // land before the barrier that follows it) both halves of fragment i
+    // after each of the first NFRAG MFMAs, so the last read has half a step
+    // to land; in K-step 1 (read by the next K-tile's first MFMAs) half i%2
+    // of fragment i/2 after MFMA i.
     auto step = [&](const i32x8 *a, const i32x8 *b, const uint32_t *wa, const uint32_t *wb, int t, int kk,
                     bool with_reads, int rsa, int rsb, int rkk, i32x8 *na, i32x8 *nb, const Op *o, bool is_a,
                     int n) {
@@ -1881,8 +1890,14 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
                 acc[ti][tj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     b[tj], a[ti], acc[ti][tj], 0, 0, 2, (int)wb[tj], 2, (int)wa[ti]);
             MFMA_FIRST();
-            if (with_reads)
+            if (with_reads && kk == 0) {
+                if (i < NFRAG) {
+                    read_frag(rsa, rsb, rkk, frag_of_slot(i), 0, na, nb);
+                    read_frag(rsa, rsb, rkk, frag_of_slot(i), 1, na, nb);
+                }
+            } else if (with_reads) {
                 read_frag(rsa, rsb, rkk, frag_of_slot(i / 2), i % 2, na, nb);
+            }
             if (o && (i % 2) == 1 && i / 2 < n) {
                 if (is_a)
                     dma_a(*o, i / 2);
@@ -1903,7 +1918,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     // load on its own (probed), so the group's words in range are intact.
     static_assert(MX_GROUP == 2 || MX_GROUP == 4, "groups of two or four K-tiles");
     const int KTP = KT < MX_GROUP ? MX_GROUP : (KT + MX_GROUP - 1) / MX_GROUP * MX_GROUP;
-    load_group(0, gw[0]);
+    load_group(0, gw[0], 0, NPA + NPB);
     // prologue DMAs: A(0), B(0), A(1), B(1)
     {
         const Op a0 = op_a(0), b0 = op_b(0), a1 = op_a(1), b1 = op_b(1);
@@ -1948,16 +1963,22 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
         after();
     };
     auto nothing = [] {};
-    // Group (kt .. kt+G-1): its first K-tile loads the next group (the last
-    // group reloads one in range; its words go unused).  The last K-tile
-    // runs like the others: its trailing DMAs are past K (no memory access)
-    // and its trailing fragment reads are never used.
+    // Group (kt .. kt+G-1): its first K-tiles load the next group (the last
+    // group reloads one in range; its words go unused) — in groups of four,
+    // the A pairs in the first K-tile and the B pairs in the second, so that
+    // fewer scattered loads stand in front of one K-tile's DMAs.  The last
+    // K-tile runs like the others: its trailing DMAs are past K (no memory
+    // access) and its trailing fragment reads are never used.
+    constexpr int SPREAD = MX_GROUP == 4 ? 2 : 1;  // K-tiles the next group's loads spread over
+    constexpr int PER = (NPA + NPB) / SPREAD;
+    static_assert((NPA + NPB) % SPREAD == 0 && SPREAD < MX_GROUP, "the loads end before the group's last K-tile");
     for (int kt = 0; kt < KTP; kt += MX_GROUP) {
-        k_tile(kt, [&] { load_group(imax(0, imin(kt + MX_GROUP, KT - 1)), gw[1]); },
-               [&] { unpack_group(gw[0], 1, kt + 1); });
+        const int tnext = imax(0, imin(kt + MX_GROUP, KT - 1));
+        k_tile(kt, [&] { load_group(tnext, gw[1], 0, PER); }, [&] { unpack_group(gw[0], 1, kt + 1); });
 #pragma unroll
         for (int j = 1; j + 1 < MX_GROUP; ++j)
-            k_tile(kt + j, nothing, [&] { unpack_group(gw[0], j + 1, kt + j + 1); });
+            k_tile(kt + j, [&] { if (j < SPREAD) load_group(tnext, gw[1], j * PER, (j + 1) * PER); },
+                   [&] { unpack_group(gw[0], j + 1, kt + j + 1); });
         k_tile(kt + MX_GROUP - 1, nothing, [&] {
 #pragma unroll
             for (int p = 0; p < NPA + NPB; ++p)
