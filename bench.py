@@ -10,8 +10,11 @@ B ~ N(0,1/K), seeded and synthetic, resident in HBM before timing starts.
                     [--dtype f16|bf16|mxf8]
 
 --dtype bf16 times tg_gemm_bf16 on the same draws; --dtype mxf8 times the
-block-scaled FP8 entry point tg_gemm_mxf8 on the same draws encoded as E4M3
-codes with one UE8M0 scale per 32 K elements (peak: the dense fp8 rate).
+block-scaled FP8 GEMM on the same draws encoded as E4M3 codes with one UE8M0
+scale per 32 K elements (peak: the dense fp8 rate): by default
+tg_gemm_mxf8_packed, with the scales converted once into the packed layout
+(tg_mx_pack_scales) before the timed region, as a caller does for a weight's
+fixed scales; --mx-scales rowmajor times tg_gemm_mxf8 on row-major scales.
 
 Prints ONE JSON line on stdout.  Timing: W untimed calls, a device
 synchronize, then K calls bracketed by HIP events recorded on the stream the
@@ -238,7 +241,7 @@ def _timed(step, steps: int, warmup: int, records: int, per_call: bool, dev, str
 
 
 def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = False,
-                  dtype: str = "f16", records: int = 1, per_call: bool = False):
+                  dtype: str = "f16", records: int = 1, per_call: bool = False, mx_scales: str = "packed"):
     import numpy as np
     import torch
 
@@ -247,7 +250,7 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
 
     dev = torch.device("cuda:0")
     if dtype == "mxf8":
-        return _time_mx(w, steps, warmup, rotate, records, per_call)
+        return _time_mx(w, steps, warmup, rotate, records, per_call, mx_scales)
     a, b = workloads.make_inputs(w, dtype=dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     A0 = torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
@@ -280,8 +283,10 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
     return dict(t, kernel=kname, tiles=tiles, a=a, b=b)
 
 
-def _time_mx(w, steps: int, warmup: int, rotate: int, records: int = 1, per_call: bool = False):
-    """time_workload for the block-scaled FP8 entry point."""
+def _time_mx(w, steps: int, warmup: int, rotate: int, records: int = 1, per_call: bool = False,
+             scales: str = "packed"):
+    """time_workload for the block-scaled FP8 entry points (packed or
+    row-major scales)."""
     import torch
 
     import dense_fp16_gemm_02_amd as tg
@@ -299,14 +304,35 @@ def _time_mx(w, steps: int, warmup: int, rotate: int, records: int = 1, per_call
     for r in range(rotate):
         sets.append(tuple(x.to(dev) for x in host) + (torch.empty((w.M, w.N), dtype=torch.float16, device=dev),))
     stream = torch.cuda.current_stream(dev)
-    st, kname, tiles = tg.tg_gemm_mxf8_plan(*sets[0], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N)
-    if st != tg.TG_OK:
-        raise RuntimeError(tg.tg_status_string(st))
+    if scales == "packed":
+        packed = []
+        for A, SA, B, SB, D in sets:
+            PA = torch.empty(tg.tg_mx_packed_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
+            PB = torch.empty(tg.tg_mx_packed_bytes(w.N, w.K), dtype=torch.uint8, device=dev)
+            for S, rows, P in ((SA, w.M, PA), (SB, w.N, PB)):
+                st = tg.tg_mx_pack_scales(S, rows, w.K, lds, P, stream)
+                if st != tg.TG_OK:
+                    raise RuntimeError(f"tg_mx_pack_scales: {tg.tg_status_string(st)}")
+            packed.append((A, PA, B, PB, D))
+        sets = packed
+        torch.cuda.synchronize(dev)
+        st, kname, tiles = tg.tg_gemm_mxf8_packed_plan(*sets[0], w.M, w.N, w.K, w.K, w.K, w.N)
+        if st != tg.TG_OK:
+            raise RuntimeError(tg.tg_status_string(st))
 
-    def step(i):
-        s = tg.tg_gemm_mxf8(*sets[i % rotate], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N, stream)
-        if s != tg.TG_OK:
-            raise RuntimeError(f"tg_gemm_mxf8: {tg.tg_status_string(s)}")
+        def step(i):
+            s = tg.tg_gemm_mxf8_packed(*sets[i % rotate], w.M, w.N, w.K, w.K, w.K, w.N, stream)
+            if s != tg.TG_OK:
+                raise RuntimeError(f"tg_gemm_mxf8_packed: {tg.tg_status_string(s)}")
+    else:
+        st, kname, tiles = tg.tg_gemm_mxf8_plan(*sets[0], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N)
+        if st != tg.TG_OK:
+            raise RuntimeError(tg.tg_status_string(st))
+
+        def step(i):
+            s = tg.tg_gemm_mxf8(*sets[i % rotate], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N, stream)
+            if s != tg.TG_OK:
+                raise RuntimeError(f"tg_gemm_mxf8: {tg.tg_status_string(s)}")
 
     t = _timed(step, steps, warmup, records, per_call, dev, stream)
     del sets
@@ -495,6 +521,9 @@ def main() -> int:
                     help="loop iterations per ceiling launch (2^20 flop per wave each)")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and print a table on stderr")
+    ap.add_argument("--mx-scales", choices=["packed", "rowmajor"], default="packed",
+                    help="with --dtype mxf8: the scale layout (packed: tg_gemm_mxf8_packed on scales packed once "
+                         "before timing; rowmajor: tg_gemm_mxf8)")
     ap.add_argument("--dtype", choices=["f16", "bf16", "mxf8"], default="f16",
                     help="element type (the headline metric is fp16; bf16 and block-scaled FP8 "
                          "are reported alongside)")
@@ -555,7 +584,7 @@ def main() -> int:
                 log(f"{ww.name:28s} (skipped: K is not whole 32-element scale blocks)")
                 continue
             r = time_workload(ww, args.steps, args.warmup, dtype=args.dtype, records=max(1, args.records),
-                              per_call=args.per_call)
+                              per_call=args.per_call, mx_scales=args.mx_scales)
             tf = ww.flop / (r["ms"] * 1e-3) / 1e12
             gbs = algorithmic_bytes(ww, args.dtype) / (r["ms"] * 1e-3) / 1e9
             pc = r["per_call_us"]
@@ -577,7 +606,7 @@ def main() -> int:
 
     vendor_line = args.vendor and not args.all and args.dtype != "mxf8"
     r = time_workload(w, args.steps, args.warmup, dtype=args.dtype, records=max(1, args.records),
-                      per_call=args.per_call, vendor=vendor_line)
+                      per_call=args.per_call, vendor=vendor_line, mx_scales=args.mx_scales)
     if vendor_line:
         r["kernel"] = "torch.matmul (vendor library; context only)"
     ms = r["ms"]
@@ -623,7 +652,8 @@ def main() -> int:
         "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "kernel": r["kernel"],
-                   "tiles": r["tiles"], "pct_of_peak": round(100 * tflops / peak, 2)},
+                   "tiles": r["tiles"], "pct_of_peak": round(100 * tflops / peak, 2),
+                   **({"mx_scales": args.mx_scales} if args.dtype == "mxf8" else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

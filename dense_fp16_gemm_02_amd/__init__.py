@@ -22,7 +22,8 @@ import os
 
 __all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_ERR_TOO_LARGE",
            "TG_ERR_LAYOUT", "TG_MFMA_F16_16X16X32", "TG_MFMA_F16_32X32X16", "TG_MFMA_BF16_16X16X32",
-           "TG_MFMA_MXF8_32X32X64", "tg_gemm_mxf8", "tg_gemm_mxf8_plan",
+           "TG_MFMA_MXF8_32X32X64", "tg_gemm_mxf8", "tg_gemm_mxf8_plan", "tg_gemm_mxf8_packed",
+           "tg_gemm_mxf8_packed_plan", "tg_mx_packed_bytes", "tg_mx_pack_scales",
            "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_gemm_bf16",
            "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "tg_mfma_ceiling", "tg_hbm_read_ceiling", "gemm"]
 
@@ -77,6 +78,14 @@ def load():
     lib.tg_gemm_mxf8.argtypes = [vp] * 5 + [i64] * 8 + [vp]
     lib.tg_gemm_mxf8_plan.restype = ctypes.c_int
     lib.tg_gemm_mxf8_plan.argtypes = [vp] * 5 + [i64] * 8 + [ctypes.c_char_p, i64, ctypes.POINTER(i64)]
+    lib.tg_gemm_mxf8_packed.restype = ctypes.c_int
+    lib.tg_gemm_mxf8_packed.argtypes = [vp] * 5 + [i64] * 6 + [vp]
+    lib.tg_gemm_mxf8_packed_plan.restype = ctypes.c_int
+    lib.tg_gemm_mxf8_packed_plan.argtypes = [vp] * 5 + [i64] * 6 + [ctypes.c_char_p, i64, ctypes.POINTER(i64)]
+    lib.tg_mx_packed_bytes.restype = i64
+    lib.tg_mx_packed_bytes.argtypes = [i64, i64]
+    lib.tg_mx_pack_scales.restype = ctypes.c_int
+    lib.tg_mx_pack_scales.argtypes = [vp, i64, i64, i64, vp, vp]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_status_string.argtypes = [ctypes.c_int]
     lib.tg_mfma_ceiling.restype = ctypes.c_int
@@ -152,6 +161,33 @@ def tg_gemm_mxf8_plan(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldsa: i
     st = load().tg_gemm_mxf8_plan(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldsa, ldb,
                                   ldsb, ldd, buf, 128, ctypes.byref(tiles))
     return st, buf.value.decode(), tiles.value
+
+
+def tg_gemm_mxf8_packed(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int,
+                        stream=None) -> int:
+    """Enqueue the block-scaled FP8 GEMM with SA and SB in the packed scale
+    layout (include/tg_gemm.h); returns the C status code."""
+    return load().tg_gemm_mxf8_packed(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldb, ldd,
+                                      _stream(stream))
+
+
+def tg_gemm_mxf8_packed_plan(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int):
+    """Host-only: (status, kernel name, output tile count) for tg_gemm_mxf8_packed."""
+    buf = ctypes.create_string_buffer(128)
+    tiles = ctypes.c_int64(0)
+    st = load().tg_gemm_mxf8_packed_plan(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldb, ldd,
+                                         buf, 128, ctypes.byref(tiles))
+    return st, buf.value.decode(), tiles.value
+
+
+def tg_mx_packed_bytes(rows: int, K: int) -> int:
+    """Bytes of the packed scale layout for ``rows`` rows and K (-1: invalid)."""
+    return load().tg_mx_packed_bytes(rows, K)
+
+
+def tg_mx_pack_scales(S, rows: int, K: int, lds: int, P, stream=None) -> int:
+    """Enqueue the row-major → packed scale conversion; returns the C status code."""
+    return load().tg_mx_pack_scales(_ptr(S), rows, K, lds, _ptr(P), _stream(stream))
 
 
 def tg_mfma_ceiling(shape: int, A, a_elems: int, B, b_elems: int, waves_per_simd: int, iters: int,

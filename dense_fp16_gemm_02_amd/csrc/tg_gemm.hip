@@ -1694,7 +1694,37 @@ struct MxGroup<4> {
     }
 };
 
-template <int BM, int BN, int WM, int WN, int MX_GROUP>
+// Where a scale word lives.  Row-major (PK false): row r's byte of block b
+// at r·lds + b, so the word of K-tile t (blocks 4t .. 4t+3) at r·lds + 4t.
+// Packed (PK true): 512-byte chunks of 32 rows × 16 blocks, chunk (r/32,
+// b/16) at (r/32)·lds + (b/16)·512 (lds = the bytes of one 32-row group:
+// 512 per 16 blocks of K), row r%32 at 16·(r%32) inside it — the
+// 32-row × scale-block atom the matrix core consumes, so that the words of
+// a 32-row fragment for four K-tiles are 512 contiguous bytes instead of 32
+// cache lines.  Offsets are relative to the tile's first row (a multiple of
+// 32).
+template <bool PK>
+__device__ inline uint32_t mx_row_off(int r, int64_t lds)
+{
+    return PK ? (uint32_t)((r >> 5) * lds + (r & 31) * 16) : (uint32_t)(r * lds);
+}
+template <bool PK>
+__device__ inline uint32_t mx_ktile_off(int t)
+{
+    return PK ? (uint32_t)((t >> 2) * 512 + (t & 3) * 4) : (uint32_t)(4 * t);
+}
+// Buffer descriptor over the scale rows of rows [r0, rows) (r0 a multiple of
+// 32): rows past `rows` read as zero words (row-major) or the packed pad.
+template <bool PK>
+__device__ inline __amdgpu_buffer_rsrc_t mx_scale_rsrc(const uint8_t *S, int r0, int rows, int64_t lds)
+{
+    const int64_t base = PK ? (int64_t)(r0 >> 5) * lds : (int64_t)r0 * lds;
+    const int64_t bytes = PK ? (int64_t)((rows + 31) / 32 - (r0 >> 5)) * lds : (int64_t)(rows - r0) * lds;
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(S + base), (short)0, (int)imin64(bytes, DMA_RANGE),
+                                             BUFFER_RSRC_WORD3);
+}
+
+template <int BM, int BN, int WM, int WN, int MX_GROUP, bool PK>
 __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ SB, _Float16 *__restrict__ D, int M, int N, int K, int64_t lda,
@@ -1784,15 +1814,11 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     };
 
     // Scale words: a buffer over the rows from m0 (n0) on, so rows past M
-    // (N), which feed only unstored outputs, read as zero words.
+    // (N), which feed only unstored outputs, read as zero words (or the
+    // packed layout's pad).
     const int srow = mx_row_of(lane), shalf = lane >> 5;
-    const __amdgpu_buffer_rsrc_t sa_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(SA + (int64_t)m0 * ldsa), (short)0, (int)imin64((int64_t)(M - m0) * ldsa, DMA_RANGE),
-        BUFFER_RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t sb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(SB + (int64_t)n0 * ldsb), (short)0, (int)imin64((int64_t)(N - n0) * ldsb, DMA_RANGE),
-        BUFFER_RSRC_WORD3);
-    const uint32_t sa_step = (uint32_t)(32 * ldsa), sb_step = (uint32_t)(32 * ldsb);
+    const __amdgpu_buffer_rsrc_t sa_rsrc = mx_scale_rsrc<PK>(SA, m0, M, ldsa);
+    const __amdgpu_buffer_rsrc_t sb_rsrc = mx_scale_rsrc<PK>(SB, n0, N, ldsb);
     uint32_t sw_a[1][TM] = {}, sw_b[1][TN] = {};  // scale words of the current K-tile
     // Grouped scale words: one MX_GROUP·4-byte load per lane per fragment
     // pair covers MX_GROUP K-tiles — lanes 0..31 take row r of the pair's
@@ -1802,8 +1828,9 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
     // a swap of the two lane halves (v_permlane32_swap) then hands every
     // lane its own fragment's word.
     constexpr int NPA = TM / 2, NPB = TN / 2;
-    const uint32_t sa_poff = (uint32_t)((wm * WTM + (lane >> 5) * 32 + srow) * ldsa);
-    const uint32_t sb_poff = (uint32_t)((wn * WTN + (lane >> 5) * 32 + srow) * ldsb);
+    const uint32_t sa_poff = mx_row_off<PK>(wm * WTM + (lane >> 5) * 32 + srow, ldsa);
+    const uint32_t sb_poff = mx_row_off<PK>(wn * WTN + (lane >> 5) * 32 + srow, ldsb);
+    const uint32_t sa_pair = mx_row_off<PK>(64, ldsa), sb_pair = mx_row_off<PK>(64, ldsb);  // 64 rows on
     using GroupWord = typename MxGroup<MX_GROUP>::type;
     GroupWord gw[2][NPA + NPB] = {};  // [current, next group][pair]
     // Pairs [lo, hi) of the group starting at K-tile t0 (A pairs first).
@@ -1811,11 +1838,11 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
 #pragma unroll
         for (int p = 0; p < NPA; ++p)
             if (p >= lo && p < hi)
-                g[p] = MxGroup<MX_GROUP>::load(sa_rsrc, (int)(sa_poff + 2 * p * sa_step + 4 * t0));
+                g[p] = MxGroup<MX_GROUP>::load(sa_rsrc, (int)(sa_poff + p * sa_pair + mx_ktile_off<PK>(t0)));
 #pragma unroll
         for (int p = 0; p < NPB; ++p)
             if (NPA + p >= lo && NPA + p < hi)
-                g[NPA + p] = MxGroup<MX_GROUP>::load(sb_rsrc, (int)(sb_poff + 2 * p * sb_step + 4 * t0));
+                g[NPA + p] = MxGroup<MX_GROUP>::load(sb_rsrc, (int)(sb_poff + p * sb_pair + mx_ktile_off<PK>(t0)));
     };
     // Words of K-tile t (index j of group g) into sw_a[0] / sw_b[0], ready
     // for the MFMA: blocks at or past K/32 (the tail of a partial last
@@ -2038,7 +2065,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
 // t+STAGES-1 (K-tiles past the end get empty ranges: no memory access), then
 // the scale words (masked to 2^0 past K/32, shifted for the lane half) and
 // two 64-K steps of two MFMAs.
-template <int STAGES>
+template <int STAGES, bool PK>
 __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ SB, _Float16 *__restrict__ D, int M, int N, int K, int64_t lda,
@@ -2090,15 +2117,10 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
     const uint8_t *a_band = A + (int64_t)m0 * lda;
     const uint8_t *b_band = B + (int64_t)n0 * ldb;
     // scale rows from row m0 of A and row n0 of B; rows past M (N) read zero
-    // words (they feed only unstored outputs)
+    // words or the packed layout's pad (they feed only unstored outputs)
     const __amdgpu_buffer_rsrc_t sc_rsrc =
-        wave == 0 ? __builtin_amdgcn_make_buffer_rsrc((void *)(SA + (int64_t)m0 * ldsa), (short)0,
-                                                      (int)imin64((int64_t)(M - m0) * ldsa, DMA_RANGE),
-                                                      BUFFER_RSRC_WORD3)
-                  : __builtin_amdgcn_make_buffer_rsrc((void *)(SB + (int64_t)n0 * ldsb), (short)0,
-                                                      (int)imin64((int64_t)(N - n0) * ldsb, DMA_RANGE),
-                                                      BUFFER_RSRC_WORD3);
-    const uint32_t sc_off = wave == 0 ? (uint32_t)(lane * ldsa) : (uint32_t)(((wave - 1) * 64 + lane) * ldsb);
+        wave == 0 ? mx_scale_rsrc<PK>(SA, m0, M, ldsa) : mx_scale_rsrc<PK>(SB, n0, N, ldsb);
+    const uint32_t sc_off = wave == 0 ? mx_row_off<PK>(lane, ldsa) : mx_row_off<PK>((wave - 1) * 64 + lane, ldsb);
 
     const int KT = (K + BKB - 1) / BKB;
     const int nblk = K / 32;
@@ -2138,7 +2160,7 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
         // into the spare slot keeps the count
         const bool first = live && wave < 3 && kt % 4 == 0;
         dma16<CPOL_CACHED>(sc_rsrc, sc_ring + (first ? slot(t) : 3) * SC_SLOT + wave * 1024,
-                           first ? sc_off + 4 * kt : DMA_OOB);
+                           first ? sc_off + mx_ktile_off<PK>(kt) : DMA_OOB);
     };
 
     const int srow = mx_row_of(lane), shalf = lane >> 5;
@@ -2621,9 +2643,15 @@ extern "C" int tg_gemm_bf16_plan(const void *A, const void *B, const void *D, in
 // has too few 256×256 tiles to occupy a quarter of the GPU.
 // The 256×256 kernel loads scale words in groups of four K-tiles when four
 // divide the K-tile count, else in pairs: two instantiations, two names.
+namespace {
+
 constexpr const char *MXF8_KERNEL_G4 = "gemm_mxf8_256x256_w2x2_g4_dma";
 constexpr const char *MXF8_KERNEL_G2 = "gemm_mxf8_256x256_w2x2_g2_dma";
 constexpr const char *MXF8_STRIP_KERNEL = "gemm_mxf8_64x128_w1x4_dma";
+// the same kernels reading scales in the packed layout
+constexpr const char *MXF8P_KERNEL_G4 = "gemm_mxf8p_256x256_w2x2_g4_dma";
+constexpr const char *MXF8P_KERNEL_G2 = "gemm_mxf8p_256x256_w2x2_g2_dma";
+constexpr const char *MXF8P_STRIP_KERNEL = "gemm_mxf8p_64x128_w1x4_dma";
 #ifndef TG_MX_STRIP_STAGES
 #define TG_MX_STRIP_STAGES 4
 #endif
@@ -2652,16 +2680,48 @@ int validate_mx(const void *A, const void *SA, const void *B, const void *SB, co
     return TG_OK;
 }
 
-extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const void *SB, void *D,
-                            int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb,
-                            int64_t ldsb, int64_t ldd, void *stream)
+// Bytes of one 32-row group of the packed scale layout: 512 per 16 blocks
+// (512 elements) of K.
+int64_t mx_packed_stride(int64_t K) { return (K + 511) / 512 * 512; }
+
+int validate_mx_packed(const void *A, const void *SA, const void *B, const void *SB, const void *D,
+                       int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd)
 {
-    int st = validate_mx(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd);
-    if (st != TG_OK)
-        return st;
-    if (M == 0 || N == 0)
-        return TG_OK;
-    st = check_device();
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldd < N)
+        return TG_ERR_INVALID_ARG;
+    if ((M > 0 && K > 0 && (!A || !SA)) || (N > 0 && K > 0 && (!B || !SB)) || (M > 0 && N > 0 && !D))
+        return TG_ERR_INVALID_ARG;
+    if (M >= LIMIT32 || N >= LIMIT32 || K >= LIMIT32 || lda >= LIMIT32 || ldb >= LIMIT32 ||
+        ldd >= LIMIT32 || 255 * lda + 128 >= DMA_RANGE || 255 * ldb + 128 >= DMA_RANGE ||
+        K >= ((int64_t)1 << 27))  // packed offsets in a workgroup's rows: < 9·K + 1024
+        return TG_ERR_TOO_LARGE;
+    if (K % 32 != 0 || lda % 16 != 0 || ldb % 16 != 0 || (uintptr_t)A % 16 != 0 || (uintptr_t)B % 16 != 0 ||
+        (uintptr_t)SA % 16 != 0 || (uintptr_t)SB % 16 != 0)
+        return TG_ERR_LAYOUT;
+    return TG_OK;
+}
+
+// The kernel a validated block-scaled problem runs on, and its workgroup count.
+const char *mx_kernel_name(int64_t M, int64_t N, int64_t K, bool packed)
+{
+    if (mx_uses_strip(M, N))
+        return packed ? MXF8P_STRIP_KERNEL : MXF8_STRIP_KERNEL;
+    if (mx_group4(K))
+        return packed ? MXF8P_KERNEL_G4 : MXF8_KERNEL_G4;
+    return packed ? MXF8P_KERNEL_G2 : MXF8_KERNEL_G2;
+}
+int64_t mx_tiles(int64_t M, int64_t N)
+{
+    return mx_uses_strip(M, N) ? mx_strip_tiles(M, N) : ((M + 255) / 256) * ((N + 255) / 256);
+}
+
+// Launch a validated, non-empty block-scaled problem; lds is the row stride
+// (row-major) or the 32-row group stride (packed) of each scale matrix.
+template <bool PK>
+int launch_mx(const void *A, const void *SA, const void *B, const void *SB, void *D, int64_t M, int64_t N,
+              int64_t K, int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd, void *stream)
+{
+    int st = check_device();
     if (st != TG_OK)
         return st;
     int Mi = (int)M, Ni = (int)N, Ki = (int)K;
@@ -2673,8 +2733,9 @@ extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const 
         int stiles_n = (int)((N + 127) / 128);
         void *sargs[] = {(void *)&A, (void *)&SA, (void *)&B, (void *)&SB, (void *)&D, &Mi, &Ni, &Ki,
                          &lda, &ldsa, &ldb, &ldsb, &ldd, &stiles_n, &dvec};
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemm_mxf8_strip_kernel<TG_MX_STRIP_STAGES>),
-                                       dim3((unsigned)sgrid), dim3(256), sargs, 0, (hipStream_t)stream);
+        hipError_t e =
+            hipLaunchKernel(reinterpret_cast<const void *>(&gemm_mxf8_strip_kernel<TG_MX_STRIP_STAGES, PK>),
+                            dim3((unsigned)sgrid), dim3(256), sargs, 0, (hipStream_t)stream);
         return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
     }
     int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
@@ -2685,10 +2746,94 @@ extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const 
                     &lda, &ldsa, &ldb, &ldsb, &ldd, &tiles_m, &tiles_n, &dvec};
     // groups of four K-tiles when they divide the K-tile count, else pairs
     // (at most one padding K-tile)
-    const void *fn = mx_group4(K) ? reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 4>)
-                                 : reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 2>);
+    const void *fn = mx_group4(K) ? reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 4, PK>)
+                                 : reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 2, PK>);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+void mx_plan_out(const char *kernel, int64_t tiles, char *name, int64_t name_len, int64_t *tiles_out)
+{
+    if (name && name_len > 0)
+        snprintf(name, (size_t)name_len, "%s", kernel);
+    if (tiles_out)
+        *tiles_out = tiles;
+}
+
+// Pack row-major scale bytes (rows × nb blocks, row stride lds) into the
+// packed layout: thread i writes the 16 bytes at 16·i, row (i / 32 / nbg)·32
+// + i % 32, blocks 16·((i / 32) % nbg) .. +15; bytes outside the matrix get
+// E8M0 127 (2^0).
+__global__ __launch_bounds__(256) void mx_pack_kernel(const uint8_t *__restrict__ S, int64_t lds, int64_t rows,
+                                                      int64_t nb, int64_t nbg, int64_t total,
+                                                      uint8_t *__restrict__ P)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total)
+        return;
+    const int64_t rr = i % 32, g = (i / 32) % nbg, rg = i / (32 * nbg);
+    const int64_t row = rg * 32 + rr;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        unsigned v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t blk = g * 16 + 4 * w + b;
+            const unsigned byte = row < rows && blk < nb ? S[row * lds + blk] : 127u;
+            v |= byte << (8 * b);
+        }
+        out[w] = v;
+    }
+    *reinterpret_cast<u32x4 *>(P + 16 * i) = out;
+}
+
+}  // namespace
+
+extern "C" int64_t tg_mx_packed_bytes(int64_t rows, int64_t K)
+{
+    if (rows < 0 || K < 0 || K % 32 != 0 || rows >= LIMIT32 || K >= LIMIT32)
+        return -1;
+    return (rows + 31) / 32 * mx_packed_stride(K);
+}
+
+extern "C" int tg_mx_pack_scales(const void *S, int64_t rows, int64_t K, int64_t lds, void *P, void *stream)
+{
+    if (rows < 0 || K < 0 || K % 32 != 0 || lds < K / 32 || (rows > 0 && K > 0 && (!S || !P)))
+        return TG_ERR_INVALID_ARG;
+    if (rows >= LIMIT32 || K >= LIMIT32 || lds >= LIMIT32)
+        return TG_ERR_TOO_LARGE;
+    if ((uintptr_t)P % 16 != 0)
+        return TG_ERR_LAYOUT;
+    if (rows == 0 || K == 0)
+        return TG_OK;
+    const int st = check_device();
+    if (st != TG_OK)
+        return st;
+    const int64_t nb = K / 32, nbg = mx_packed_stride(K) / 512, total = (rows + 31) / 32 * nbg * 32;
+    const int64_t grid = (total + 255) / 256;
+    if (grid >= LIMIT32)
+        return TG_ERR_TOO_LARGE;
+    const uint8_t *s = static_cast<const uint8_t *>(S);
+    uint8_t *p = static_cast<uint8_t *>(P);
+    int64_t lds_ = lds, rows_ = rows;
+    void *args[] = {(void *)&s, &lds_, &rows_, (void *)&nb, (void *)&nbg, (void *)&total, (void *)&p};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&mx_pack_kernel), dim3((unsigned)grid), dim3(256),
+                                   args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const void *SB, void *D,
+                            int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb,
+                            int64_t ldsb, int64_t ldd, void *stream)
+{
+    int st = validate_mx(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd);
+    if (st != TG_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    return launch_mx<false>(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd, stream);
 }
 
 extern "C" int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, const void *SB,
@@ -2697,18 +2842,35 @@ extern "C" int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, c
                                  int64_t name_len, int64_t *tiles)
 {
     int st = validate_mx(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd);
-    if (name && name_len > 0)
-        name[0] = 0;
-    if (tiles)
-        *tiles = 0;
+    mx_plan_out("", 0, name, name_len, tiles);
     if (st != TG_OK || M == 0 || N == 0)
         return st;
-    const bool strip = mx_uses_strip(M, N);
-    if (name && name_len > 0)
-        snprintf(name, (size_t)name_len, "%s",
-                 strip ? MXF8_STRIP_KERNEL : mx_group4(K) ? MXF8_KERNEL_G4 : MXF8_KERNEL_G2);
-    if (tiles)
-        *tiles = strip ? mx_strip_tiles(M, N) : ((M + 255) / 256) * ((N + 255) / 256);
+    mx_plan_out(mx_kernel_name(M, N, K, false), mx_tiles(M, N), name, name_len, tiles);
+    return TG_OK;
+}
+
+extern "C" int tg_gemm_mxf8_packed(const void *A, const void *SA, const void *B, const void *SB, void *D,
+                                   int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
+                                   void *stream)
+{
+    int st = validate_mx_packed(A, SA, B, SB, D, M, N, K, lda, ldb, ldd);
+    if (st != TG_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    const int64_t stride = mx_packed_stride(K);
+    return launch_mx<true>(A, SA, B, SB, D, M, N, K, lda, stride, ldb, stride, ldd, stream);
+}
+
+extern "C" int tg_gemm_mxf8_packed_plan(const void *A, const void *SA, const void *B, const void *SB,
+                                        const void *D, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                        int64_t ldb, int64_t ldd, char *name, int64_t name_len, int64_t *tiles)
+{
+    int st = validate_mx_packed(A, SA, B, SB, D, M, N, K, lda, ldb, ldd);
+    mx_plan_out("", 0, name, name_len, tiles);
+    if (st != TG_OK || M == 0 || N == 0)
+        return st;
+    mx_plan_out(mx_kernel_name(M, N, K, true), mx_tiles(M, N), name, name_len, tiles);
     return TG_OK;
 }
 

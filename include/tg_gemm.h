@@ -40,9 +40,11 @@ enum {
      * K, lda, ldb, ldd must be below 2^31, and A, B, D must each span fewer
      * than 2^62 elements).  Nothing is launched. */
     TG_ERR_TOO_LARGE = -4,
-    /* tg_gemm_mxf8 only: K is not a multiple of 32, lda or ldb not a
-     * multiple of 16, ldsa or ldsb not a multiple of 4, A or B not 16-byte
-     * aligned, or SA or SB not 4-byte aligned.  Nothing is launched. */
+    /* block-scaled entry points only: K is not a multiple of 32, lda or
+     * ldb not a multiple of 16, ldsa or ldsb not a multiple of 4, A or B
+     * not 16-byte aligned, or SA or SB not 4-byte aligned (16-byte for the
+     * packed layout; tg_mx_pack_scales: P not 16-byte aligned).  Nothing is
+     * launched. */
     TG_ERR_LAYOUT = -5
 };
 
@@ -159,6 +161,63 @@ int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, const void *
                       int64_t M, int64_t N, int64_t K,
                       int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd,
                       char *name, int64_t name_len, int64_t *tiles);
+
+/*
+ * Packed scale layout.  The page's scale-factor layout ("TIRx Layout API",
+ * section "Scale Factor 布局") is built from an atom of 32 rows × the scale
+ * factors one MMA reads, repeated along M and along the K scale blocks.
+ * The packed layout stores scales the same way in device memory: 512-byte
+ * chunks of 32 rows × 16 blocks (512 elements of K), so that the scale
+ * bytes a 32-row operand fragment needs for four 128-K tiles are 512
+ * contiguous bytes rather than one cache line per row.  For R rows and K
+ * (a multiple of 32), with G = ceil(K/512) chunks per 32-row group:
+ *
+ *   byte of row r, block b  at  ((r/32)·G + b/16)·512 + (r%32)·16 + b%16
+ *
+ * and the buffer holds ceil(R/32)·G·512 bytes (tg_mx_packed_bytes).  Bytes
+ * for rows >= R or blocks >= K/32 are never used (tg_mx_pack_scales writes
+ * 127 there).
+ *
+ * tg_mx_packed_bytes — the size of that buffer for `rows` rows and K; -1 if
+ * rows or K is negative, K is not a multiple of 32, or either is >= 2^31.
+ */
+int64_t tg_mx_packed_bytes(int64_t rows, int64_t K);
+
+/*
+ * tg_mx_pack_scales — enqueue the conversion of row-major scales (rows ×
+ * K/32 bytes, row r at S + r·lds, as tg_gemm_mxf8 takes them) into the
+ * packed layout at P (device memory of tg_mx_packed_bytes(rows, K) bytes,
+ * 16-byte aligned, not overlapping S).  A layout change only: every byte
+ * is copied unchanged.  Returns TG_OK (nothing to do for rows == 0 or
+ * K == 0), TG_ERR_INVALID_ARG (negative sizes, K not a multiple of 32,
+ * lds < K/32, a NULL pointer with bytes behind it), TG_ERR_LAYOUT (P not
+ * 16-byte aligned), TG_ERR_TOO_LARGE (rows, K or lds >= 2^31),
+ * TG_ERR_DEVICE or TG_ERR_LAUNCH.  Asynchronous on `stream`.
+ */
+int tg_mx_pack_scales(const void *S, int64_t rows, int64_t K, int64_t lds, void *P, void *stream);
+
+/*
+ * tg_gemm_mxf8_packed — tg_gemm_mxf8 with both scale matrices in the packed
+ * layout (SA for M rows, SB for N rows, each 16-byte aligned; no scale
+ * leading dimensions).  Same arithmetic, the same kernels (they differ only
+ * in where a scale word is read), so D is bit-identical to tg_gemm_mxf8 on
+ * the same scales.  A caller whose scales are fixed (a weight's) packs them
+ * once; the block-scaled kernels then read each fragment's scale words for
+ * four K-tiles from 512 contiguous bytes.  Arguments, ownership and status
+ * codes as for tg_gemm_mxf8; TG_ERR_LAYOUT also when SA or SB is not
+ * 16-byte aligned; TG_ERR_TOO_LARGE also for K >= 2^27 (the packed
+ * offsets inside one workgroup's rows stay below 2^31).
+ */
+int tg_gemm_mxf8_packed(const void *A, const void *SA, const void *B, const void *SB, void *D,
+                        int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
+                        void *stream);
+
+/* tg_gemm_mxf8_packed_plan — host-only: the kernel name ("gemm_mxf8p_…")
+ * and tile count tg_gemm_mxf8_packed would use, and its validation status;
+ * outputs as for tg_gemm_f16_plan. */
+int tg_gemm_mxf8_packed_plan(const void *A, const void *SA, const void *B, const void *SB, const void *D,
+                             int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
+                             char *name, int64_t name_len, int64_t *tiles);
 
 /* tg_status_string — a static, NUL-terminated description of a status. */
 const char *tg_status_string(int status);

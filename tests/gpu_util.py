@@ -82,10 +82,27 @@ def _bytes(x: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to("cuda:0")
 
 
-def run_mx(a, sa, b, sb, M, N, K, guard=0, label=""):
+def pack_scales(S, rows, K, lds):
+    """The packed scale layout of a device buffer of row-major scales (rows ×
+    lds bytes), made on the device by tg_mx_pack_scales."""
+    import torch
+
+    import dense_fp16_gemm_02_amd as tg
+
+    nbytes = tg.tg_mx_packed_bytes(rows, K)
+    assert nbytes >= 0
+    P = torch.full((max(nbytes, 16),), 0xA5, dtype=torch.uint8, device="cuda:0")
+    st = tg.tg_mx_pack_scales(S, rows, K, lds, P, torch.cuda.current_stream())
+    assert st == tg.TG_OK, st
+    return P
+
+
+def run_mx(a, sa, b, sb, M, N, K, guard=0, label="", packed=False):
     """D (M, N) fp16 window and the full (M+2g, N+2g) buffer (uint16) of
     tg_gemm_mxf8 on byte arrays a (M, lda), sa (M, ldsa), b (N, ldb), sb
-    (N, ldsb); every byte in them is passed to the device as is."""
+    (N, ldsb); every byte in them is passed to the device as is.  With
+    packed=True the scales are first converted on the device into the packed
+    layout (tg_mx_pack_scales) and tg_gemm_mxf8_packed runs instead."""
     import torch
 
     import dense_fp16_gemm_02_amd as tg
@@ -95,8 +112,13 @@ def run_mx(a, sa, b, sb, M, N, K, guard=0, label=""):
     A, SA, B, SB = _bytes(a), _bytes(sa), _bytes(b), _bytes(sb)
     d = torch.full(((M + 2 * guard) * ldd + 8,), SENTINEL, dtype=torch.int16, device="cuda:0")
     dptr = d.data_ptr() + 2 * (guard * ldd + guard)
-    say(f"mxf8 {label} M={M} N={N} K={K} lda={lda} ldsa={ldsa} ldb={ldb} ldsb={ldsb} guard={guard}")
-    st = tg.tg_gemm_mxf8(A, SA, B, SB, dptr, M, N, K, lda, ldsa, ldb, ldsb, ldd, torch.cuda.current_stream())
+    say(f"mxf8 {label} M={M} N={N} K={K} lda={lda} ldsa={ldsa} ldb={ldb} ldsb={ldsb} guard={guard} "
+        f"packed={packed}")
+    if packed:
+        PA, PB = pack_scales(SA, M, K, ldsa), pack_scales(SB, N, K, ldsb)
+        st = tg.tg_gemm_mxf8_packed(A, PA, B, PB, dptr, M, N, K, lda, ldb, ldd, torch.cuda.current_stream())
+    else:
+        st = tg.tg_gemm_mxf8(A, SA, B, SB, dptr, M, N, K, lda, ldsa, ldb, ldsb, ldd, torch.cuda.current_stream())
     torch.cuda.synchronize()
     full = d.cpu().numpy().view(np.uint16)[:(M + 2 * guard) * ldd].reshape(M + 2 * guard, ldd)
     win = np.array(full[guard:guard + M, guard:guard + N].view(np.float16))

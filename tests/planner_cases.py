@@ -84,6 +84,9 @@ MX_CASES: dict[str, Case] = {
     "gemm_mxf8_256x256_w2x2_g2_dma": Case(2100, 2060, 384),
 }
 
+# the same kernels reading scales in the packed layout (tg_gemm_mxf8_packed)
+MXP_CASES: dict[str, Case] = {n.replace("gemm_mxf8_", "gemm_mxf8p_"): c for n, c in MX_CASES.items()}
+
 TILES = sorted({t for t, _ in _F16_BF16})
 PATHS = ("dma", "vec", "scalar")
 DMA_ONLY = {"256x256_w2x2_pers", "128x128_w2x2_ws"}  # kernels only on the direct-to-LDS path

@@ -226,3 +226,45 @@ def test_ceiling_codes_and_validation():
                                  (FAKE + 4, 1 << 20, 256, FAKE), (FAKE, 1 << 20, 0, FAKE),
                                  (FAKE, 1 << 20, 256, None)]:
         assert tg.tg_hbm_read_ceiling(src, nbytes, wg, out) == tg.TG_ERR_INVALID_ARG
+
+
+def test_packed_scale_entry_points_validation():
+    """The packed-scale entry points: buffer sizes, kernel names, and every
+    rejection before a device is touched."""
+    assert tg.tg_mx_packed_bytes(0, 4096) == 0
+    assert tg.tg_mx_packed_bytes(1, 32) == 512
+    assert tg.tg_mx_packed_bytes(32, 512) == 512
+    assert tg.tg_mx_packed_bytes(33, 512) == 1024
+    assert tg.tg_mx_packed_bytes(64, 544) == 2048
+    assert tg.tg_mx_packed_bytes(8192, 4096) == 256 * 8 * 512
+    for rows, K in [(-1, 32), (4, 33), (4, -32), (1 << 31, 32)]:
+        assert tg.tg_mx_packed_bytes(rows, K) == -1
+    names = {}
+    for w in workloads.WORKLOADS:
+        K = w.K - w.K % 32
+        st, name, tiles = tg.tg_gemm_mxf8_packed_plan(FAKE, FAKE, FAKE, FAKE, FAKE, w.M, w.N, K, K, K, w.N)
+        assert st == tg.TG_OK
+        names[w.name] = name
+    assert names["linear_8192x14336x4096"] == "gemm_mxf8p_256x256_w2x2_g4_dma"
+    assert names["skinny_64x28672x8192"] == "gemm_mxf8p_64x128_w1x4_dma"
+    ok = dict(A=FAKE, SA=FAKE, B=FAKE, SB=FAKE, D=FAKE, M=300, N=300, K=128, lda=128, ldb=128, ldd=300)
+    for kw, want in [({"K": 100, "lda": 112, "ldb": 112}, tg.TG_ERR_LAYOUT), ({"lda": 136}, tg.TG_ERR_LAYOUT),
+                     ({"SA": FAKE + 4}, tg.TG_ERR_LAYOUT), ({"SB": FAKE + 8}, tg.TG_ERR_LAYOUT),
+                     ({"A": FAKE + 8}, tg.TG_ERR_LAYOUT), ({"M": -1}, tg.TG_ERR_INVALID_ARG),
+                     ({"lda": 96}, tg.TG_ERR_INVALID_ARG), ({"ldd": 299}, tg.TG_ERR_INVALID_ARG),
+                     ({"SA": None}, tg.TG_ERR_INVALID_ARG), ({"D": None}, tg.TG_ERR_INVALID_ARG),
+                     ({"K": 1 << 27, "lda": 1 << 27, "ldb": 1 << 27}, tg.TG_ERR_TOO_LARGE),
+                     ({"M": 1 << 31}, tg.TG_ERR_TOO_LARGE)]:
+        p = {**ok, **kw}
+        args = [p[k] for k in ("A", "SA", "B", "SB", "D", "M", "N", "K", "lda", "ldb", "ldd")]
+        assert tg.tg_gemm_mxf8_packed(*args, None) == want, kw
+        st, name, tiles = tg.tg_gemm_mxf8_packed_plan(*args)
+        assert st == want and name == "" and tiles == 0, kw
+    # the pack: argument checks, and nothing to do for empty matrices
+    assert tg.tg_mx_pack_scales(FAKE, 4, 33, 4, FAKE, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_mx_pack_scales(FAKE, 4, 128, 3, FAKE, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_mx_pack_scales(None, 4, 128, 4, FAKE, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_mx_pack_scales(FAKE, -1, 128, 4, FAKE, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_mx_pack_scales(FAKE, 4, 128, 4, FAKE + 4, None) == tg.TG_ERR_LAYOUT
+    assert tg.tg_mx_pack_scales(FAKE, 1 << 31, 128, 4, FAKE, None) == tg.TG_ERR_TOO_LARGE
+    assert tg.tg_mx_pack_scales(None, 0, 128, 4, None, None) == tg.TG_OK

@@ -1,7 +1,8 @@
 """Every kernel instantiation the public entry points can launch, on the GPU.
 
 For each name in ``planner_cases.CASES`` (fp16 and bf16: every tile × load
-path) and ``planner_cases.MX_CASES`` (block-scaled FP8), one launch through
+path) and ``planner_cases.MX_CASES`` / ``MXP_CASES`` (block-scaled FP8, row-major
+and packed scales), one launch through
 the C ABI whose plan must be that name, compared with the oracle on every
 element and bit for bit: the operands are integer-valued (fp16: the index
 pattern, |D| <= 6K, exact for K <= 341; bf16: values in {-1, 0, 1}, exact for
@@ -18,7 +19,7 @@ import pytest
 import oracle
 import workloads
 from gpu_util import NAN_BITS, SENTINEL, run_mx, say
-from planner_cases import CASES, MX_CASES
+from planner_cases import CASES, MX_CASES, MXP_CASES
 
 torch = pytest.importorskip("torch")
 tg = pytest.importorskip("dense_fp16_gemm_02_amd")
@@ -82,9 +83,10 @@ def test_instantiation_exact(name):
 ONE, MINUS_ONE, ZERO = 0x38, 0xb8, 0x00
 
 
-@pytest.mark.parametrize("name", sorted(MX_CASES))
+@pytest.mark.parametrize("name", sorted(MX_CASES) + sorted(MXP_CASES))
 def test_mx_instantiation_exact(name):
-    c = MX_CASES[name]
+    packed = name in MXP_CASES
+    c = MXP_CASES[name] if packed else MX_CASES[name]
     M, N, K = c.M, c.N, c.K
     rng = np.random.default_rng(K + M)
     codes = np.array([ONE, MINUS_ONE, ZERO], np.uint8)
@@ -94,10 +96,14 @@ def test_mx_instantiation_exact(name):
     ld = max(4, (nb + 3) // 4 * 4)
     sa = workloads.pad_bytes(rng.integers(124, 131, size=(M, nb)).astype(np.uint8), ld, 0xff)
     sb = workloads.pad_bytes(rng.integers(124, 131, size=(N, nb)).astype(np.uint8), ld, 0xff)
-    st, planned, _ = tg.tg_gemm_mxf8_plan(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
-                                          M, N, K, K, ld, K, ld, N)
+    if packed:
+        st, planned, _ = tg.tg_gemm_mxf8_packed_plan(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+                                                     M, N, K, K, K, N)
+    else:
+        st, planned, _ = tg.tg_gemm_mxf8_plan(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+                                              M, N, K, K, ld, K, ld, N)
     assert st == tg.TG_OK and planned == name, (planned, name)
-    d, _, st = run_mx(a, sa, b, sb, M, N, K, label=f"coverage {name}")
+    d, _, st = run_mx(a, sa, b, sb, M, N, K, label=f"coverage {name}", packed=packed)
     assert st == tg.TG_OK
     res = oracle.gemm_mx(a, sa, b, sb, M, N, K)
     assert np.array_equal(d.view(np.uint16), res.d.view(np.uint16))

@@ -12,7 +12,7 @@ import itertools
 
 import pytest
 
-from planner_cases import CASES, MX_CASES, all_fp_names, vec_lda
+from planner_cases import CASES, MX_CASES, MXP_CASES, all_fp_names, vec_lda
 
 tg = pytest.importorskip("dense_fp16_gemm_02_amd")
 
@@ -34,6 +34,12 @@ def test_every_case_plans_to_its_name():
         nb = c.K // 32
         ld = max(4, (nb + 3) // 4 * 4)
         st, got, _ = tg.tg_gemm_mxf8_plan(BASE, BASE, BASE, BASE, BASE, c.M, c.N, c.K, c.K, ld, c.K, ld, c.N)
+        assert st == tg.TG_OK and got == name, (name, c)
+
+
+def test_packed_cases_plan_to_their_names():
+    for name, c in MXP_CASES.items():
+        st, got, _ = tg.tg_gemm_mxf8_packed_plan(BASE, BASE, BASE, BASE, BASE, c.M, c.N, c.K, c.K, c.K, c.N)
         assert st == tg.TG_OK and got == name, (name, c)
 
 
@@ -63,7 +69,10 @@ def test_mx_planner_sweep_stays_inside_the_table():
         st, name, _ = tg.tg_gemm_mxf8_plan(BASE, BASE, BASE, BASE, BASE, M, N, K, K, ld, K, ld, N)
         assert st == tg.TG_OK and name in MX_CASES, (M, N, K, name)
         seen.add(name)
-    assert seen == set(MX_CASES)
+        st, pname, _ = tg.tg_gemm_mxf8_packed_plan(BASE, BASE, BASE, BASE, BASE, M, N, K, K, K, N)
+        assert st == tg.TG_OK and pname == name.replace("gemm_mxf8_", "gemm_mxf8p_"), (M, N, K, pname)
+        seen.add(pname)
+    assert seen == set(MX_CASES) | set(MXP_CASES)
 
 
 def test_persistent_kernel_conditions():
