@@ -492,6 +492,38 @@ def algorithmic_bytes(w, dtype: str) -> int:
     return w.min_bytes
 
 
+def run_processes(args) -> int:
+    """--processes P: run this benchmark line in P independent processes
+    (each its own warm-up and timed calls) and report the median process
+    with every process's time beside it.  The CPU baseline, if asked for,
+    runs in the last process only."""
+    import subprocess
+    import statistics
+
+    argv = [a for a in sys.argv[1:]]
+    i = argv.index("--processes") if "--processes" in argv else -1
+    if i >= 0:
+        del argv[i:i + 2]
+    argv = [a for a in argv if not a.startswith("--processes=")]
+    lines = []
+    for p in range(args.processes):
+        extra = [] if p == args.processes - 1 else ["--no-cpu-baseline"]
+        out = subprocess.run([sys.executable, os.path.abspath(__file__), *argv, *extra],
+                             stdout=subprocess.PIPE, text=True)
+        if out.returncode != 0:
+            return out.returncode
+        lines.append(json.loads(out.stdout.strip().splitlines()[-1]))
+        log(f"process {p}: {lines[-1]['ms_per_step'] * 1e3:.2f} us per step")
+    order = sorted(range(len(lines)), key=lambda k: lines[k]["ms_per_step"])
+    line = dict(lines[order[len(order) // 2]])
+    line["cpu_baseline"] = lines[-1].get("cpu_baseline")
+    line["processes_ms_per_step"] = [round(x["ms_per_step"], 6) for x in lines]
+    line["processes"] = args.processes
+    log(f"median of {args.processes} processes: {statistics.median(x['ms_per_step'] for x in lines) * 1e3:.2f} us")
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,6 +553,9 @@ def main() -> int:
                     help="loop iterations per ceiling launch (2^20 flop per wave each)")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and print a table on stderr")
+    ap.add_argument("--processes", type=int, default=1,
+                    help="run the line in P independent processes and report the median process "
+                         "(not with --all)")
     ap.add_argument("--mx-scales", choices=["packed", "rowmajor"], default="packed",
                     help="with --dtype mxf8: the scale layout (packed: tg_gemm_mxf8_packed on scales packed once "
                          "before timing; rowmajor: tg_gemm_mxf8)")
@@ -553,6 +588,12 @@ def main() -> int:
             print("--traffic-record needs --copy-bytes and --traffic-kernel", file=sys.stderr)
             return 2
         return traffic_record(args)
+
+    if args.processes > 1:
+        if args.all or args.mfma_ceiling or args.hbm_ceiling or args.copy_bytes:
+            print("--processes applies to the single benchmark line only", file=sys.stderr)
+            return 2
+        return run_processes(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

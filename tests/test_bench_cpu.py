@@ -90,3 +90,13 @@ def test_trace_summary_orders_dispatches_and_averages_the_timed_window(tmp_path)
     t = bench.trace_summary(str(p), "gemm_", (1, 4))
     assert t["per_call_us"] == [1.0, 3.0, 5.0, 7.0, 9.0]
     assert t["calls"] == 5 and t["window_mean_us"] == 5.0 and t["mean_us"] == 5.0
+
+
+def test_processes_only_for_the_single_line(capsys, monkeypatch):
+    """--processes runs the one benchmark line in independent processes; it is
+    refused with --all and the measurement-only modes (before any process or
+    device is started)."""
+    for extra in (["--all"], ["--mfma-ceiling"], ["--hbm-ceiling"]):
+        monkeypatch.setattr(sys, "argv", ["bench.py", "--processes", "3", *extra])
+        assert bench.main() == 2
+        assert "single benchmark line" in capsys.readouterr().err
