@@ -67,8 +67,11 @@ enum {
  * There is no alpha/beta: D's prior contents are ignored.  Any alignment is
  * accepted; 16-byte-aligned A/B with K, lda, ldb multiples of 8 take the
  * vector-load path, other inputs a slower element-wise path with the same
- * results.  The library allocates nothing, keeps no state between calls and
- * is safe to call from several host threads.  Kernel faults surface at the
+ * results.  The library allocates nothing, keeps no state between calls
+ * (beyond a per-device cache of the device's attributes) and is safe to
+ * call from several host threads.  A call only launches kernels — no
+ * allocation, memset or synchronization — so it may be recorded into a HIP
+ * graph under stream capture and replayed.  Kernel faults surface at the
  * caller's next synchronization.
  *
  * Returns TG_OK, TG_ERR_INVALID_ARG, TG_ERR_TOO_LARGE, TG_ERR_DEVICE or
