@@ -3,7 +3,7 @@
  * matrix cores sustain on their own, with no memory traffic, and the rate a
  * streaming read of HBM reaches.
  *
- * The GEMMs of tg_gemm.h are judged against the dense matrix-core peaks
+ * The GEMMs of tg_gemm.h are measured against the dense matrix-core peaks
  * (fp16 and bf16 2.5 PFLOP/s, fp8 5 PFLOP/s).  Those peaks assume the
  * shader clock at its maximum; with random operands
  * the power limit lowers the clock, and a kernel doing nothing but matrix
