@@ -1328,18 +1328,19 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
 // the other in K-step 1, after the barrier that drains its stage.
 //
 // Epilogue, at the last K-tile of a tile, with no workgroup barrier: the
-// 3-stage operand's stage of that K-tile is free until the next tile's
-// second K-step, and the 2-stage operand's refill is held back until the
-// epilogue is done, so both drained stages (64 KiB) hold the staging of
-// D.  Each wave stages its 128×128 block in two 64-row halves of 16 KiB, in
-// exactly the 1 KiB pieces of those two stages that its own DMAs fill (a
-// DMA instruction of wave w writes the piece 4p + w of a stage), so the
-// only later writers of its staging memory are its own DMAs, issued after
-// its own staging reads have completed.  Per half: fp32 → element RNE into
-// LDS (16-byte chunk index XORed with the row), read back 16 bytes per lane
-// along rows, store whole row segments; the accumulators are cleared as
-// they are read.  Then the held-back refill is issued and the next tile's
-// first K-step runs on fragments read before the epilogue.
+// 3-stage operand's stage of that K-tile is drained at that K-tile's
+// barrier and refilled only in the next tile's first K-step, so it holds
+// the staging of D (32 KiB), while the other operand's refill goes out in
+// that K-tile as in every other one (its data has the whole epilogue to
+// land).  Each wave stages its 128×128 block in four 32-row quarters of 8
+// KiB, in exactly the eight 1 KiB pieces of that stage that its own DMAs
+// fill (a DMA instruction of wave w writes the piece 4p + w of a stage), so
+// the only later writers of its staging memory are its own DMAs, issued
+// after its own staging reads have completed.  Per quarter: fp32 → element
+// RNE into LDS (16-byte chunk index XORed with the row), read back 16 bytes
+// per lane along rows, store whole row segments; the accumulators are
+// cleared as they are read.  Then the next tile's first K-step runs on
+// fragments read before the epilogue.
 //
 // RS0: fragment reads of K-step 0 every RS0-th MFMA slot (2: in the first
 // half of the step, so they have landed by the barrier's wait; 4: spread).
@@ -1491,28 +1492,30 @@ __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
     constexpr int X3 = SA == 3 ? 1 : 2;  // operand with three stages: refilled in K-step 0
     constexpr int Y2 = 3 - X3;           // the other: refilled in K-step 1
 
-    // Staged epilogue of tile `ti`, using stage sa of A and stage sb of B.
+    // Staged epilogue of tile `ti` in the three-stage operand's stage sa
+    // (A) or sb (B).
+    static_assert(TM % 4 == 0 && WTM / 4 * WTN == 8 * PIECE, "a quarter of a wave block fills its eight pieces");
     auto epilogue = [&](int ti, int sa, int sb) __attribute__((always_inline)) {
         int tm, tn;
         my_tile(ti, tm, tn);
         const int row0 = tm * BM + wm * WTM, col0 = tn * BN + wn * WTN;
-        E *const st_a = a_ring + sa * STAGE + wave * PIECE;  // this wave's pieces: +4·PIECE apart
-        E *const st_b = b_ring + sb * STAGE + wave * PIECE;
-        // piece q (0..15) of the half: rows 4q..4q+3, 256 bytes each
-        auto piece = [&](int q) { return q < 8 ? st_a + q * 4 * PIECE : st_b + (q - 8) * 4 * PIECE; };
+        // this wave's pieces, 4·PIECE apart; piece q (0..7) of a quarter holds
+        // its rows 4q..4q+3, 256 bytes each
+        E *const st = (X3 == 1 ? a_ring + sa * STAGE : b_ring + sb * STAGE) + wave * PIECE;
+        auto piece = [&](int q) { return st + q * 4 * PIECE; };
         int l = lane_id();
         asm volatile("" : "+v"(l));  // opaque: the lane terms below are not hoisted out of the tile loop
         const int fr = l & 15, fh = l >> 4;     // accumulator lane: D row fr, columns 4·fh..4·fh+3
         const int rr = l >> 4, rc = l & 15;     // store lane: row rr of a piece, 16-byte chunk rc
         const bool inside = dvec && row0 + WTM <= M && col0 + WTN <= N;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 4; ++h) {
 #pragma unroll
-            for (int i = 0; i < TM / 2; ++i)
+            for (int i = 0; i < TM / 4; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const f32x4 v = acc[4 * h + i][j];
-                    acc[4 * h + i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    const f32x4 v = acc[2 * h + i][j];
+                    acc[2 * h + i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                     V4 e;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -1521,24 +1524,20 @@ __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
                     E *dst = piece(4 * i + (fr >> 2)) + (fr & 3) * (WTN) + (((c >> 3) ^ fr) << 3) + (c & 7);
                     *reinterpret_cast<V4 *>(dst) = e;
                 }
-            const int rbase = row0 + 64 * h;
+            const int rbase = row0 + 32 * h;
             const int col = col0 + 8 * rc;
             if (inside) {
                 E *dst = D + (int64_t)(rbase + rr) * ldd + col;
+                V8 v[8];  // all eight LDS reads ahead of the stores
 #pragma unroll
-                for (int q0 = 0; q0 < 16; q0 += 8) {  // LDS reads in batches of 8 ahead of the stores
-                    V8 v[8];
+                for (int q = 0; q < 8; ++q)
+                    v[q] = *reinterpret_cast<const V8 *>(piece(q) + rr * WTN + ((rc ^ ((4 * q + rr) & 15)) << 3));
 #pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        v[q] = *reinterpret_cast<const V8 *>(piece(q0 + q) + rr * WTN +
-                                                             ((rc ^ ((4 * (q0 + q) + rr) & 15)) << 3));
-#pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        *reinterpret_cast<V8 *>(dst + (int64_t)(4 * (q0 + q)) * ldd) = v[q];
-                }
+                for (int q = 0; q < 8; ++q)
+                    *reinterpret_cast<V8 *>(dst + (int64_t)(4 * q) * ldd) = v[q];
             } else {
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
+                for (int q = 0; q < 8; ++q) {
                     const V8 v = *reinterpret_cast<const V8 *>(piece(q) + rr * WTN + ((rc ^ ((4 * q + rr) & 15)) << 3));
                     const int row = rbase + 4 * q + rr;
                     if (row < M) {
@@ -1579,42 +1578,31 @@ __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
     // One K-tile: K-step 0 with the three-stage operand's refill (K-tile dk
     // of the DMA stream's tile), the wait for the next K-tile and the
     // barrier that drains this one's stages, K-step 1 with the other
-    // operand's refill (unless `hold`: the caller issues it after the
-    // epilogue) reading K-step 0 of the next K-tile (unless `last`).
-    auto k_tile = [&](int dk, bool live, bool hold, bool last) __attribute__((always_inline)) {
+    // operand's refill, reading K-step 0 of the next K-tile (unless `last`).
+    auto k_tile = [&](int dk, bool live, bool last) __attribute__((always_inline)) {
         step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], X3, dma_rsrc(X3 == 1 ? a_src : b_src, dk, live),
              rs0_t{});
         wait_vmem<PASSES>();  // all but that refill: the next K-tile has landed (this wave's part)
         barrier_lds();        // ... for every wave; this K-tile's stages are drained
         const int sa1 = sa + 1 == SA ? 0 : sa + 1, sb1 = sb + 1 == SB ? 0 : sb + 1;
-        step(fa[1], fb[1], !last, sa1, sb1, 0, fa[0], fb[0], hold ? 0 : Y2,
-             dma_rsrc(Y2 == 1 ? a_src : b_src, dk, live), rs4_t{});
-        if (!hold)
-            next_dma_stage();
+        step(fa[1], fb[1], !last, sa1, sb1, 0, fa[0], fb[0], Y2, dma_rsrc(Y2 == 1 ? a_src : b_src, dk, live),
+             rs4_t{});
+        next_dma_stage();
         sa = sa1;
         sb = sb1;
     };
     for (int ci = 0; ci < mine; ++ci) {
         for (int kt = 0; kt + 2 < KT; ++kt)
-            k_tile(kt + 2, true, false, false);
+            k_tile(kt + 2, true, false);
         // the last two K-tiles refill K-tiles 0 and 1 of the next tile
         const bool more = ci + 1 < mine;
         if (more)
             set_dma_tile(ci + 1);
-        k_tile(0, more, false, false);
+        k_tile(0, more, false);
         const int esa = sa, esb = sb;  // stages of the last K-tile: the staging memory
-        k_tile(1, more, true, !more);
+        k_tile(1, more, !more);
         epilogue(ci, esa, esb);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging reads are done
-        const auto r = dma_rsrc(Y2 == 1 ? a_src : b_src, 1, more);
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            if (Y2 == 1)
-                dma_a(r, p);
-            else
-                dma_b(r, p);
-        }
-        next_dma_stage();
     }
     wait_vmem<0>();  // no DMA or store may be outstanding when the wave ends
 }
