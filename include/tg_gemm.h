@@ -72,7 +72,9 @@ enum {
  * call from several host threads.  A call only launches kernels — no
  * allocation, memset or synchronization — so it may be recorded into a HIP
  * graph under stream capture and replayed.  Kernel faults surface at the
- * caller's next synchronization.
+ * caller's next synchronization.  From 4 MiB of D on (16-byte aligned rows),
+ * most of D is written with non-temporal stores: it is not kept in the
+ * caches for a consumer that reads it right after the call.
  *
  * Returns TG_OK, TG_ERR_INVALID_ARG, TG_ERR_TOO_LARGE, TG_ERR_DEVICE or
  * TG_ERR_LAUNCH.
