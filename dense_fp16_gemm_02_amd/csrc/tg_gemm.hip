@@ -1375,7 +1375,9 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
 // RNE into LDS (16-byte chunk index XORed with the row), read back 16 bytes
 // per lane along rows, store whole row segments; the accumulators are
 // cleared as they are read.  Then the next tile's first K-step runs on
-// fragments read before the epilogue.
+// fragments read before the epilogue.  The wave waits for all its DMAs
+// before its first store, so the next tile's first K-tile needs no wait
+// and the stores drain behind it.
 //
 // RS0: fragment reads of K-step 0 every RS0-th MFMA slot (2: in the first
 // half of the step, so they have landed by the barrier's wait; 4: spread).
@@ -1559,6 +1561,12 @@ __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
                     E *dst = piece(4 * i + (fr >> 2)) + (fr & 3) * (WTN) + (((c >> 3) ^ fr) << 3) + (c & 7);
                     *reinterpret_cast<V4 *>(dst) = e;
                 }
+            // Every DMA of this wave has landed before its first store:
+            // the vector-memory counter also counts stores, so the next
+            // tile's first wait, which only needs those DMAs, is dropped
+            // instead of draining this epilogue's stores.
+            if (h == 0)
+                wait_vmem<0>();
             const int rbase = row0 + 32 * h;
             const int col = col0 + 8 * rc;
             if (inside) {
@@ -1622,10 +1630,13 @@ __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
     // of the DMA stream's tile), the wait for the next K-tile and the
     // barrier that drains this one's stages, K-step 1 with the other
     // operand's refill, reading K-step 0 of the next K-tile (unless `last`).
+    bool fresh = false;  // the first K-tile after an epilogue, whose next K-tile landed before the stores
     auto k_tile = [&](int dk, bool live, bool last) __attribute__((always_inline)) {
         step(fa[0], fb[0], true, sa, sb, 1, fa[1], fb[1], X3, dma_rsrc(X3 == 1 ? a_src : b_src, dk, live),
              rs0_t{});
-        wait_vmem<PASSES>();  // all but that refill: the next K-tile has landed (this wave's part)
+        if (!fresh)
+            wait_vmem<PASSES>();  // all but that refill: the next K-tile has landed (this wave's part)
+        fresh = false;
         barrier_lds();        // ... for every wave; this K-tile's stages are drained
         const int sa1 = sa + 1 == SA ? 0 : sa + 1, sb1 = sb + 1 == SB ? 0 : sb + 1;
         step(fa[1], fb[1], !last, sa1, sb1, 0, fa[0], fb[0], Y2, dma_rsrc(Y2 == 1 ? a_src : b_src, dk, live),
@@ -1646,6 +1657,7 @@ __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
         k_tile(1, more, !more);
         epilogue(ci, esa, esb);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging reads are done
+        fresh = true;
     }
     wait_vmem<0>();  // no DMA or store may be outstanding when the wave ends
 }
