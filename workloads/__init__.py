@@ -65,7 +65,15 @@ WORKLOADS = [
              ("normal", 0.0, 1.0), ("normal", 0.0, 1.0 / np.sqrt(8192.0))),
 ]
 
-BY_NAME = {w.name: w for w in WORKLOADS}
+# Shapes profiled besides the five workloads, one per kernel those do not
+# reach: 2048³ runs the producer/consumer 128×128 kernel.  The same recipe
+# as the linear layer (A ~ N(0,1), B ~ N(0,1/K)).
+EXTRA_WORKLOADS = [
+    Workload(5, "mid_2048x2048x2048", 2048, 2048, 2048,
+             ("normal", 0.0, 1.0), ("normal", 0.0, 1.0 / np.sqrt(2048.0))),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def _draw64(rng: np.random.Generator, shape, dist) -> np.ndarray:
