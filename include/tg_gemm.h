@@ -148,8 +148,9 @@ int tg_gemm_bf16_plan(const void *A, const void *B, const void *D,
  *   ldsa, ldsb bytes between scale rows, >= K/32 and multiples of 4.
  *   stream     as for tg_gemm_f16.
  *
- * Ownership, threading, asynchrony and edge cases in M and N are as for
- * tg_gemm_f16.  Returns TG_OK, TG_ERR_INVALID_ARG (negative sizes, a
+ * Ownership, threading, asynchrony, edge cases in M and N and the
+ * non-temporal writing of a large D are as for tg_gemm_f16.  Returns TG_OK,
+ * TG_ERR_INVALID_ARG (negative sizes, a
  * leading dimension too small, a NULL pointer with elements behind it),
  * TG_ERR_LAYOUT (the multiple-of and alignment rules above),
  * TG_ERR_TOO_LARGE, TG_ERR_DEVICE or TG_ERR_LAUNCH.
