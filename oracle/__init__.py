@@ -76,8 +76,13 @@ def _load():
     lib.oracle_e4m3_to_double_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
     lib.oracle_e8m0_to_double.restype = ctypes.c_double
     lib.oracle_e8m0_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e5m2_to_double_array.restype = None
+    lib.oracle_e5m2_to_double_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
     lib.oracle_gemm_mxf8.restype = ctypes.c_int
     lib.oracle_gemm_mxf8.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 7 + [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+    lib.oracle_gemm_mx.restype = ctypes.c_int
+    lib.oracle_gemm_mx.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 7 + [ctypes.c_int] * 2 + [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
     for fn in (lib.oracle_gemm_f16, lib.oracle_gemm_bf16):
         fn.restype = ctypes.c_int
@@ -132,6 +137,18 @@ def e4m3_to_double(b: np.ndarray) -> np.ndarray:
     out = np.empty(b.shape, dtype=np.float64)
     _load().oracle_e4m3_to_double_array(b.ctypes.data, out.ctypes.data, b.size)
     return out
+
+
+def e5m2_to_double(b: np.ndarray) -> np.ndarray:
+    """Exact FP8 E5M2 (uint8 codes) → float64 decode (±inf for 0x7c, 0xfc;
+    NaN for the other codes with all exponent bits set)."""
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_e5m2_to_double_array(b.ctypes.data, out.ctypes.data, b.size)
+    return out
+
+
+MX_FORMATS = {"e4m3": 0, "e5m2": 1}
 
 
 def e8m0_to_double(s: np.ndarray) -> np.ndarray:
@@ -207,11 +224,15 @@ def gemm(a: np.ndarray, b: np.ndarray, M: int, N: int, K: int,
 
 
 def gemm_mx(a: np.ndarray, sa: np.ndarray, b: np.ndarray, sb: np.ndarray, M: int, N: int, K: int,
-            rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None) -> Result:
-    """Reference block-scaled FP8 GEMM on uint8 arrays: ``a`` (M×lda E4M3
-    codes), ``sa`` (M×ldsa UE8M0 scale bytes, one per 32 K elements), and
-    likewise ``b``, ``sb`` for the N rows of B.  Returns fp16 D for the
-    requested rows with the float64 sum and bound beside it."""
+            rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None,
+            a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> Result:
+    """Reference block-scaled FP8 GEMM on uint8 arrays: ``a`` (M×lda FP8
+    codes in the encoding ``a_fmt``, "e4m3" or "e5m2"), ``sa`` (M×ldsa UE8M0
+    scale bytes, one per 32 K elements), and likewise ``b``, ``sb`` for the N
+    rows of B.  Returns fp16 D for the requested rows with the float64 sum
+    and bound beside it."""
+    if a_fmt not in MX_FORMATS or b_fmt not in MX_FORMATS:
+        raise ValueError("element encodings are 'e4m3' or 'e5m2'")
     a = np.ascontiguousarray(a, dtype=np.uint8)
     b = np.ascontiguousarray(b, dtype=np.uint8)
     sa = np.ascontiguousarray(sa, dtype=np.uint8)
@@ -233,9 +254,9 @@ def gemm_mx(a: np.ndarray, sa: np.ndarray, b: np.ndarray, sb: np.ndarray, M: int
     total = np.zeros((nrows, N), dtype=np.float64)
     nt = default_threads() if nthreads is None else nthreads
     ptr = lambda x: x.ctypes.data if x.size else None
-    rc = _load().oracle_gemm_mxf8(
+    rc = _load().oracle_gemm_mx(
         ptr(a), ptr(sa), ptr(b), ptr(sb), ptr(d), ptr(bound), ptr(total),
-        M, N, K, lda, ldsa, ldb, ldsb,
+        M, N, K, lda, ldsa, ldb, ldsb, MX_FORMATS[a_fmt], MX_FORMATS[b_fmt],
         rows_arr.ctypes.data if rows_arr is not None and rows_arr.size else None, nrows, nt)
     if rc != 0:
         raise ValueError("oracle rejected its arguments")

@@ -27,9 +27,10 @@
  * pages do not name the output rounding for BF16; the reading taken is the
  * fp16 one, round-to-nearest-even, applied directly from the float64 sum.
  *
- * Block-scaled FP8 variant (oracle_gemm_mxf8, at the end of this file): FP8
- * E4M3 operands with one 8-bit power-of-two scale per 32 K elements of a row,
- * fp16 output; its definition and readings are written out there.
+ * Block-scaled FP8 variant (oracle_gemm_mx and oracle_gemm_mxf8, at the end
+ * of this file): FP8 E4M3 or E5M2 operands with one 8-bit power-of-two scale
+ * per 32 K elements of a row, fp16 output; its definition and readings are
+ * written out there.
  */
 #include <math.h>
 #include <pthread.h>
@@ -318,6 +319,14 @@ int oracle_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *D,
  * with A[i,k] = A[i*lda+k], SA[i,b] = SA[i*ldsa+b] (bytes), likewise B, SB.
  * Every term is exact in float64 (two 4-bit significands and powers of two
  * within float64's range); the sum is taken in increasing k.
+ *
+ * OCP MX also defines the FP8 element encoding E5M2 (sign, 5 exponent bits
+ * with bias 15, 2 fraction bits, with infinities: exponent 31 is ±infinity
+ * for fraction 0 and NaN otherwise; largest finite 57344).  oracle_gemm_mx
+ * takes the encoding of A and of B separately (0 E4M3, 1 E5M2); an infinite
+ * element times a zero one gives NaN and infinities propagate through the
+ * sum as IEEE float64 arithmetic has them, and the result rounds to a signed
+ * infinity when it exceeds binary16's range, as for the fp16 GEMM.
  */
 
 /* E4M3 → float64, exact: exponent 0 is the subnormal range f·2^-9, otherwise
@@ -337,6 +346,23 @@ double oracle_e4m3_to_double(uint8_t b)
     return sign ? -v : v;
 }
 
+/* E5M2 → float64, exact: exponent 31 is ±infinity (fraction 0) or NaN,
+ * exponent 0 the subnormal range f·2^-16, otherwise (4+f)·2^(e-17). */
+double oracle_e5m2_to_double(uint8_t b)
+{
+    int sign = (b >> 7) & 1;
+    int e = (b >> 2) & 31;
+    int f = b & 3;
+    double v;
+    if (e == 31)
+        v = f == 0 ? INFINITY : NAN;
+    else if (e == 0)
+        v = ldexp((double)f, -16);
+    else
+        v = ldexp((double)(4 | f), e - 17);
+    return sign ? -v : v;
+}
+
 /* UE8M0 scale byte → float64: 2^(s-127), NaN for 255. */
 double oracle_e8m0_to_double(uint8_t s)
 {
@@ -349,6 +375,12 @@ void oracle_e4m3_to_double_array(const uint8_t *b, double *out, int64_t n)
         out[i] = oracle_e4m3_to_double(b[i]);
 }
 
+void oracle_e5m2_to_double_array(const uint8_t *b, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e5m2_to_double(b[i]);
+}
+
 struct mx_job {
     const uint8_t *A, *SA, *B, *SB;
     uint16_t *D;
@@ -356,7 +388,7 @@ struct mx_job {
     int64_t N, K, lda, ldsa, ldb, ldsb;
     const int64_t *rows;
     int64_t r_begin, r_end;
-    const double *elut, *slut;
+    const double *alut, *blut, *slut;
 };
 
 static void *run_rows_mx(void *p)
@@ -371,8 +403,8 @@ static void *run_rows_mx(void *p)
             const uint8_t *sb = jb->SB + j * jb->ldsb;
             double s = 0.0, bnd = 0.0;
             for (int64_t k = 0; k < jb->K; ++k) {
-                double x = jb->slut[sa[k / 32]] * jb->elut[a[k]];
-                double y = jb->slut[sb[k / 32]] * jb->elut[b[k]];
+                double x = jb->slut[sa[k / 32]] * jb->alut[a[k]];
+                double y = jb->slut[sb[k / 32]] * jb->blut[b[k]];
                 s += x * y;
                 bnd += fabs(x) * fabs(y);
             }
@@ -390,15 +422,18 @@ static void *run_rows_mx(void *p)
 
 /* Reference block-scaled GEMM; rows, outputs, threads and the return value as
  * for oracle_gemm_f16.  ldsa and ldsb count scale bytes per row and must
- * cover ceil(K/32) blocks. */
-int oracle_gemm_mxf8(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
-                     uint16_t *D, double *bound, double *sum,
-                     int64_t M, int64_t N, int64_t K,
-                     int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb,
-                     const int64_t *rows, int64_t nrows, int nthreads)
+ * cover ceil(K/32) blocks; a_fmt and b_fmt are the element encodings of A
+ * and B (0 E4M3, 1 E5M2). */
+int oracle_gemm_mx(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
+                   uint16_t *D, double *bound, double *sum,
+                   int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int a_fmt, int b_fmt,
+                   const int64_t *rows, int64_t nrows, int nthreads)
 {
     const int64_t blocks = (K + 31) / 32;
     if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldsa < blocks || ldsb < blocks || nrows < 0)
+        return -1;
+    if (a_fmt < 0 || a_fmt > 1 || b_fmt < 0 || b_fmt > 1)
         return -1;
     if (!rows && nrows != M)
         return -1;
@@ -409,9 +444,10 @@ int oracle_gemm_mxf8(const uint8_t *A, const uint8_t *SA, const uint8_t *B, cons
     if (nrows == 0 || N == 0)
         return 0;
 
-    double elut[256], slut[256];
+    double alut[256], blut[256], slut[256];
     for (int v = 0; v < 256; ++v) {
-        elut[v] = oracle_e4m3_to_double((uint8_t)v);
+        alut[v] = a_fmt ? oracle_e5m2_to_double((uint8_t)v) : oracle_e4m3_to_double((uint8_t)v);
+        blut[v] = b_fmt ? oracle_e5m2_to_double((uint8_t)v) : oracle_e4m3_to_double((uint8_t)v);
         slut[v] = oracle_e8m0_to_double((uint8_t)v);
     }
     if (nthreads < 1)
@@ -429,7 +465,7 @@ int oracle_gemm_mxf8(const uint8_t *A, const uint8_t *SA, const uint8_t *B, cons
     for (int t = 0; t < nthreads; ++t) {
         int64_t cnt = per + (t < extra ? 1 : 0);
         struct mx_job jb = {A, SA, B, SB, D, bound, sum, N, K, lda, ldsa, ldb, ldsb, rows,
-                            start, start + cnt, elut, slut};
+                            start, start + cnt, alut, blut, slut};
         jobs[t] = jb;
         start += cnt;
     }
@@ -447,4 +483,15 @@ int oracle_gemm_mxf8(const uint8_t *A, const uint8_t *SA, const uint8_t *B, cons
     free(th);
     free(jobs);
     return 0;
+}
+
+/* E4M3 on both operands. */
+int oracle_gemm_mxf8(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
+                     uint16_t *D, double *bound, double *sum,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb,
+                     const int64_t *rows, int64_t nrows, int nthreads)
+{
+    return oracle_gemm_mx(A, SA, B, SB, D, bound, sum, M, N, K, lda, ldsa, ldb, ldsb, 0, 0, rows, nrows,
+                          nthreads);
 }

@@ -245,12 +245,18 @@ def make_mx_inputs(w: Workload):
     return qa, sa, qb, sb
 
 
-def random_mx(seed: int, rows: int, K: int, scale_lo: int = 120, scale_hi: int = 134):
-    """Seeded random E4M3 codes (every finite code, both signs, NaN codes
-    excluded) with random scale bytes in [scale_lo, scale_hi]."""
+def random_mx(seed: int, rows: int, K: int, scale_lo: int = 120, scale_hi: int = 134, fmt: str = "e4m3"):
+    """Seeded random FP8 codes (every finite code of the encoding ``fmt``,
+    "e4m3" or "e5m2", both signs; NaN and infinity codes excluded) with random
+    scale bytes in [scale_lo, scale_hi]."""
     rng = np.random.Generator(np.random.PCG64(seed))
     codes = rng.integers(0, 256, size=(rows, K)).astype(np.uint8)
-    codes = np.where((codes & 0x7f) == 0x7f, codes ^ np.uint8(1), codes).astype(np.uint8)
+    if fmt == "e4m3":
+        codes = np.where((codes & 0x7f) == 0x7f, codes ^ np.uint8(1), codes).astype(np.uint8)
+    elif fmt == "e5m2":  # exponent field 31 (infinity, NaN) moved down to 30
+        codes = np.where((codes & 0x7c) == 0x7c, codes ^ np.uint8(0x04), codes).astype(np.uint8)
+    else:
+        raise ValueError("fmt is 'e4m3' or 'e5m2'")
     scales = rng.integers(scale_lo, scale_hi + 1, size=(rows, (K + MX_BLOCK - 1) // MX_BLOCK)).astype(np.uint8)
     return codes, scales
 
