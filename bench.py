@@ -241,7 +241,8 @@ def _timed(step, steps: int, warmup: int, records: int, per_call: bool, dev, str
 
 
 def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = False,
-                  dtype: str = "f16", records: int = 1, per_call: bool = False, mx_scales: str = "packed"):
+                  dtype: str = "f16", records: int = 1, per_call: bool = False, mx_scales: str = "packed",
+                  mx_formats=("e4m3", "e4m3")):
     import numpy as np
     import torch
 
@@ -250,7 +251,7 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
 
     dev = torch.device("cuda:0")
     if dtype == "mxf8":
-        return _time_mx(w, steps, warmup, rotate, records, per_call, mx_scales)
+        return _time_mx(w, steps, warmup, rotate, records, per_call, mx_scales, mx_formats)
     a, b = workloads.make_inputs(w, dtype=dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     A0 = torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
@@ -284,9 +285,10 @@ def time_workload(w, steps: int, warmup: int, rotate: int = 2, vendor: bool = Fa
 
 
 def _time_mx(w, steps: int, warmup: int, rotate: int, records: int = 1, per_call: bool = False,
-             scales: str = "packed"):
+             scales: str = "packed", formats=("e4m3", "e4m3")):
     """time_workload for the block-scaled FP8 entry points (packed or
-    row-major scales)."""
+    row-major scales; element encodings ``formats`` of A and B: E4M3 on both
+    times tg_gemm_mxf8(_packed), any other pair tg_gemm_mx(_packed))."""
     import torch
 
     import dense_fp16_gemm_02_amd as tg
@@ -295,7 +297,8 @@ def _time_mx(w, steps: int, warmup: int, rotate: int, records: int = 1, per_call
     if w.K % 32:
         raise RuntimeError(f"{w.name}: K = {w.K} is not whole 32-element scale blocks")
     dev = torch.device("cuda:0")
-    qa, sa, qb, sb = workloads.make_mx_inputs(w)
+    qa, sa, qb, sb = workloads.make_mx_inputs(w, *formats)
+    fa, fb = (tg.TG_MX_E5M2 if f == "e5m2" else tg.TG_MX_E4M3 for f in formats)
     nb = w.K // 32
     lds = (nb + 3) // 4 * 4  # scale rows padded to whole 4-byte words (the entry point's rule)
     host = [torch.from_numpy(x) for x in (qa, workloads.pad_bytes(sa, lds, 127), qb,
@@ -316,23 +319,34 @@ def _time_mx(w, steps: int, warmup: int, rotate: int, records: int = 1, per_call
             packed.append((A, PA, B, PB, D))
         sets = packed
         torch.cuda.synchronize(dev)
-        st, kname, tiles = tg.tg_gemm_mxf8_packed_plan(*sets[0], w.M, w.N, w.K, w.K, w.K, w.N)
-        if st != tg.TG_OK:
-            raise RuntimeError(tg.tg_status_string(st))
+        if fa == fb == tg.TG_MX_E4M3:
+            st, kname, tiles = tg.tg_gemm_mxf8_packed_plan(*sets[0], w.M, w.N, w.K, w.K, w.K, w.N)
 
-        def step(i):
-            s = tg.tg_gemm_mxf8_packed(*sets[i % rotate], w.M, w.N, w.K, w.K, w.K, w.N, stream)
-            if s != tg.TG_OK:
-                raise RuntimeError(f"tg_gemm_mxf8_packed: {tg.tg_status_string(s)}")
+            def call(i):
+                return tg.tg_gemm_mxf8_packed(*sets[i % rotate], w.M, w.N, w.K, w.K, w.K, w.N, stream)
+        else:
+            st, kname, tiles = tg.tg_gemm_mx_packed_plan(*sets[0], w.M, w.N, w.K, w.K, w.K, w.N, fa, fb)
+
+            def call(i):
+                return tg.tg_gemm_mx_packed(*sets[i % rotate], w.M, w.N, w.K, w.K, w.K, w.N, fa, fb, stream)
     else:
-        st, kname, tiles = tg.tg_gemm_mxf8_plan(*sets[0], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N)
-        if st != tg.TG_OK:
-            raise RuntimeError(tg.tg_status_string(st))
+        if fa == fb == tg.TG_MX_E4M3:
+            st, kname, tiles = tg.tg_gemm_mxf8_plan(*sets[0], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N)
 
-        def step(i):
-            s = tg.tg_gemm_mxf8(*sets[i % rotate], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N, stream)
-            if s != tg.TG_OK:
-                raise RuntimeError(f"tg_gemm_mxf8: {tg.tg_status_string(s)}")
+            def call(i):
+                return tg.tg_gemm_mxf8(*sets[i % rotate], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N, stream)
+        else:
+            st, kname, tiles = tg.tg_gemm_mx_plan(*sets[0], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N, fa, fb)
+
+            def call(i):
+                return tg.tg_gemm_mx(*sets[i % rotate], w.M, w.N, w.K, w.K, lds, w.K, lds, w.N, fa, fb, stream)
+    if st != tg.TG_OK:
+        raise RuntimeError(tg.tg_status_string(st))
+
+    def step(i):
+        s = call(i)
+        if s != tg.TG_OK:
+            raise RuntimeError(f"{kname}: {tg.tg_status_string(s)}")
 
     t = _timed(step, steps, warmup, records, per_call, dev, stream)
     del sets
@@ -340,7 +354,7 @@ def _time_mx(w, steps: int, warmup: int, rotate: int, records: int = 1, per_call
     return dict(t, kernel=kname, tiles=tiles, a=(qa, sa), b=(qb, sb))
 
 
-def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16"):
+def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16", mx_formats=("e4m3", "e4m3")):
     """Time the oracle on the first R rows of D (all N columns, full K)."""
     import numpy as np
 
@@ -348,7 +362,8 @@ def cpu_baseline(w, a, b, seconds: float, rows_override=None, fmt: str = "f16"):
 
     def ref(rows, threads):
         if fmt == "mxf8":
-            return oracle.gemm_mx(a[0], a[1], b[0], b[1], w.M, w.N, w.K, rows=rows, nthreads=threads)
+            return oracle.gemm_mx(a[0], a[1], b[0], b[1], w.M, w.N, w.K, rows=rows, nthreads=threads,
+                                  a_fmt=mx_formats[0], b_fmt=mx_formats[1])
         return oracle.gemm(a, b, w.M, w.N, w.K, rows=rows, nthreads=threads, fmt=fmt)
 
     threads = oracle.default_threads()
@@ -559,6 +574,10 @@ def main() -> int:
     ap.add_argument("--mx-scales", choices=["packed", "rowmajor"], default="packed",
                     help="with --dtype mxf8: the scale layout (packed: tg_gemm_mxf8_packed on scales packed once "
                          "before timing; rowmajor: tg_gemm_mxf8)")
+    ap.add_argument("--mx-formats", choices=["e4m3,e4m3", "e5m2,e5m2", "e5m2,e4m3", "e4m3,e5m2"],
+                    default="e4m3,e4m3",
+                    help="with --dtype mxf8: the element encodings of A and B (OCP MX FP8: E4M3 or E5M2; "
+                         "anything but E4M3 on both times tg_gemm_mx / tg_gemm_mx_packed)")
     ap.add_argument("--dtype", choices=["f16", "bf16", "mxf8"], default="f16",
                     help="element type (the headline metric is fp16; bf16 and block-scaled FP8 "
                          "are reported alongside)")
@@ -611,6 +630,8 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     w = workloads.BY_NAME[args.workload]
+    mx_formats = tuple(args.mx_formats.split(","))
+    mx_elem = "E4M3" if mx_formats == ("e4m3", "e4m3") else "×".join(f.upper() for f in mx_formats)
 
     if args.mfma_ceiling:
         return mfma_ceiling(w, args)
@@ -625,7 +646,7 @@ def main() -> int:
                 log(f"{ww.name:28s} (skipped: K is not whole 32-element scale blocks)")
                 continue
             r = time_workload(ww, args.steps, args.warmup, dtype=args.dtype, records=max(1, args.records),
-                              per_call=args.per_call, mx_scales=args.mx_scales)
+                              per_call=args.per_call, mx_scales=args.mx_scales, mx_formats=mx_formats)
             tf = ww.flop / (r["ms"] * 1e-3) / 1e12
             gbs = algorithmic_bytes(ww, args.dtype) / (r["ms"] * 1e-3) / 1e9
             pc = r["per_call_us"]
@@ -647,7 +668,8 @@ def main() -> int:
 
     vendor_line = args.vendor and not args.all and args.dtype != "mxf8"
     r = time_workload(w, args.steps, args.warmup, dtype=args.dtype, records=max(1, args.records),
-                      per_call=args.per_call, vendor=vendor_line, mx_scales=args.mx_scales)
+                      per_call=args.per_call, vendor=vendor_line, mx_scales=args.mx_scales,
+                      mx_formats=mx_formats)
     if vendor_line:
         r["kernel"] = "torch.matmul (vendor library; context only)"
     ms = r["ms"]
@@ -658,7 +680,7 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, r["a"], r["b"], args.cpu_seconds, args.cpu_rows, args.dtype)
+        cpu = cpu_baseline(w, r["a"], r["b"], args.cpu_seconds, args.cpu_rows, args.dtype, mx_formats)
         log(f"cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
     traffic = measured_traffic(r["kernel"], w.name)
@@ -666,7 +688,7 @@ def main() -> int:
     metric = {
         "f16": f"TFLOP/s fp16 GEMM D=A·B^T at {shape}; % of MFMA dense fp16 peak",
         "bf16": f"TFLOP/s bf16 GEMM D=A·B^T at {shape}; % of MFMA dense bf16 peak",
-        "mxf8": f"TFLOP/s block-scaled FP8 GEMM D=(SA·A)·(SB·B)^T (E4M3, UE8M0 per 32 K) at {shape}; "
+        "mxf8": f"TFLOP/s block-scaled FP8 GEMM D=(SA·A)·(SB·B)^T ({mx_elem}, UE8M0 per 32 K) at {shape}; "
                 f"% of MFMA dense fp8 peak",
     }[args.dtype]
     # a contraction below the ridge point is bounded by HBM, not the matrix cores
@@ -694,7 +716,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "kernel": r["kernel"],
                    "tiles": r["tiles"], "pct_of_peak": round(100 * tflops / peak, 2),
-                   **({"mx_scales": args.mx_scales} if args.dtype == "mxf8" else {})},
+                   **({"mx_scales": args.mx_scales} if args.dtype == "mxf8" else {}),
+                   **({"mx_formats": args.mx_formats} if args.dtype == "mxf8" and mx_formats != ("e4m3", "e4m3")
+                      else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -24,9 +24,13 @@ __all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_
            "TG_ERR_LAYOUT", "TG_MFMA_F16_16X16X32", "TG_MFMA_F16_32X32X16", "TG_MFMA_BF16_16X16X32",
            "TG_MFMA_MXF8_32X32X64", "tg_gemm_mxf8", "tg_gemm_mxf8_plan", "tg_gemm_mxf8_packed",
            "tg_gemm_mxf8_packed_plan", "tg_mx_packed_bytes", "tg_mx_pack_scales",
+           "TG_MX_E4M3", "TG_MX_E5M2", "tg_gemm_mx", "tg_gemm_mx_plan", "tg_gemm_mx_packed",
+           "tg_gemm_mx_packed_plan",
            "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_gemm_bf16",
            "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "tg_mfma_ceiling", "tg_hbm_read_ceiling", "gemm"]
 
+TG_MX_E4M3 = 0  # block-scaled element encodings (include/tg_gemm.h)
+TG_MX_E5M2 = 1
 TG_OK = 0
 TG_ERR_INVALID_ARG = -1
 TG_ERR_LAUNCH = -2
@@ -82,6 +86,16 @@ def load():
     lib.tg_gemm_mxf8_packed.argtypes = [vp] * 5 + [i64] * 6 + [vp]
     lib.tg_gemm_mxf8_packed_plan.restype = ctypes.c_int
     lib.tg_gemm_mxf8_packed_plan.argtypes = [vp] * 5 + [i64] * 6 + [ctypes.c_char_p, i64, ctypes.POINTER(i64)]
+    ci = ctypes.c_int
+    lib.tg_gemm_mx.restype = ctypes.c_int
+    lib.tg_gemm_mx.argtypes = [vp] * 5 + [i64] * 8 + [ci, ci, vp]
+    lib.tg_gemm_mx_plan.restype = ctypes.c_int
+    lib.tg_gemm_mx_plan.argtypes = [vp] * 5 + [i64] * 8 + [ci, ci, ctypes.c_char_p, i64, ctypes.POINTER(i64)]
+    lib.tg_gemm_mx_packed.restype = ctypes.c_int
+    lib.tg_gemm_mx_packed.argtypes = [vp] * 5 + [i64] * 6 + [ci, ci, vp]
+    lib.tg_gemm_mx_packed_plan.restype = ctypes.c_int
+    lib.tg_gemm_mx_packed_plan.argtypes = [vp] * 5 + [i64] * 6 + [ci, ci, ctypes.c_char_p, i64,
+                                                                    ctypes.POINTER(i64)]
     lib.tg_mx_packed_bytes.restype = i64
     lib.tg_mx_packed_bytes.argtypes = [i64, i64]
     lib.tg_mx_pack_scales.restype = ctypes.c_int
@@ -177,6 +191,41 @@ def tg_gemm_mxf8_packed_plan(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, 
     tiles = ctypes.c_int64(0)
     st = load().tg_gemm_mxf8_packed_plan(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldb, ldd,
                                          buf, 128, ctypes.byref(tiles))
+    return st, buf.value.decode(), tiles.value
+
+
+def tg_gemm_mx(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldsa: int, ldb: int, ldsb: int,
+               ldd: int, a_format: int, b_format: int, stream=None) -> int:
+    """tg_gemm_mxf8 with the element encodings of A and B chosen separately
+    (TG_MX_E4M3 or TG_MX_E5M2); returns the C status code."""
+    return load().tg_gemm_mx(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldsa, ldb, ldsb,
+                             ldd, a_format, b_format, _stream(stream))
+
+
+def tg_gemm_mx_plan(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldsa: int, ldb: int, ldsb: int,
+                    ldd: int, a_format: int, b_format: int):
+    """Host-only: (status, kernel name, output tile count) for tg_gemm_mx."""
+    buf = ctypes.create_string_buffer(128)
+    tiles = ctypes.c_int64(0)
+    st = load().tg_gemm_mx_plan(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldsa, ldb, ldsb,
+                                ldd, a_format, b_format, buf, 128, ctypes.byref(tiles))
+    return st, buf.value.decode(), tiles.value
+
+
+def tg_gemm_mx_packed(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int,
+                      a_format: int, b_format: int, stream=None) -> int:
+    """tg_gemm_mxf8_packed with the element encodings chosen separately."""
+    return load().tg_gemm_mx_packed(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldb, ldd,
+                                    a_format, b_format, _stream(stream))
+
+
+def tg_gemm_mx_packed_plan(A, SA, B, SB, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int,
+                           a_format: int, b_format: int):
+    """Host-only: (status, kernel name, output tile count) for tg_gemm_mx_packed."""
+    buf = ctypes.create_string_buffer(128)
+    tiles = ctypes.c_int64(0)
+    st = load().tg_gemm_mx_packed_plan(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(D), M, N, K, lda, ldb, ldd,
+                                       a_format, b_format, buf, 128, ctypes.byref(tiles))
     return st, buf.value.decode(), tiles.value
 
 

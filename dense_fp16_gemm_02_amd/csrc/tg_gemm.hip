@@ -1713,6 +1713,13 @@ __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// Element encodings (OCP MX defines two for FP8): FMT = a + 2·b with a, b the
+// encodings of A and B, 0 for E4M3 and 1 for E5M2 (the instruction's format
+// codes for fp8 and bf8).  The scaled MFMA takes the format of its first
+// source (here B, as the MFMA inputs are swapped) and of its second (A).
+#define MX_FMT_A(F) ((F) & 1)
+#define MX_FMT_B(F) ((F) >> 1)
+
 __host__ __device__ constexpr int mx_row_of(int l) { return l & 31; }
 __host__ __device__ constexpr int mx_chunk_of(int l, int kk, int half) { return 4 * kk + 2 * half + (l >> 5); }
 constexpr bool mx_fragment_covers_k_step()
@@ -1782,7 +1789,7 @@ __device__ inline __amdgpu_buffer_rsrc_t mx_scale_rsrc(const uint8_t *S, int r0,
                                              BUFFER_RSRC_WORD3);
 }
 
-template <int BM, int BN, int WM, int WN, int MX_GROUP, bool PK>
+template <int BM, int BN, int WM, int WN, int MX_GROUP, bool PK, int FMT>
 __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ SB, _Float16 *__restrict__ D, int M, int N, int K, int64_t lda,
@@ -1970,10 +1977,10 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
             // the scale byte of K-step kk is byte 2·kk of the prepared word
             if (kk == 0)
                 acc[ti][tj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    b[tj], a[ti], acc[ti][tj], 0, 0, 0, (int)wb[tj], 0, (int)wa[ti]);
+                    b[tj], a[ti], acc[ti][tj], MX_FMT_B(FMT), MX_FMT_A(FMT), 0, (int)wb[tj], 0, (int)wa[ti]);
             else
                 acc[ti][tj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    b[tj], a[ti], acc[ti][tj], 0, 0, 2, (int)wb[tj], 2, (int)wa[ti]);
+                    b[tj], a[ti], acc[ti][tj], MX_FMT_B(FMT), MX_FMT_A(FMT), 2, (int)wb[tj], 2, (int)wa[ti]);
             MFMA_FIRST();
             if (with_reads && kk == 0) {
                 if (i < NFRAG) {
@@ -2126,7 +2133,7 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
 // t+STAGES-1 (K-tiles past the end get empty ranges: no memory access), then
 // the scale words (masked to 2^0 past K/32, shifted for the lane half) and
 // two 64-K steps of two MFMAs.
-template <int STAGES, bool PK>
+template <int STAGES, bool PK, int FMT>
 __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ SB, _Float16 *__restrict__ D, int M, int N, int K, int64_t lda,
@@ -2304,10 +2311,12 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
                 for (int j = 0; j < TN; ++j) {
                     if (kk == 0)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fb[j], fa[i], acc[i][j], 0, 0, 0, (int)wb[j], 0, (int)wa[i]);
+                            fb[j], fa[i], acc[i][j], MX_FMT_B(FMT), MX_FMT_A(FMT), 0, (int)wb[j], 0,
+                            (int)wa[i]);
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fb[j], fa[i], acc[i][j], 0, 0, 2, (int)wb[j], 2, (int)wa[i]);
+                            fb[j], fa[i], acc[i][j], MX_FMT_B(FMT), MX_FMT_A(FMT), 2, (int)wb[j], 2,
+                            (int)wa[i]);
                 }
         }
     }
@@ -2775,6 +2784,12 @@ int validate_mx_packed(const void *A, const void *SA, const void *B, const void 
     return TG_OK;
 }
 
+// Name suffix of the element encodings FMT (none for E4M3 on both operands).
+const char *mx_fmt_suffix(int fmt)
+{
+    return fmt == 1 ? "_e5m2xe4m3" : fmt == 2 ? "_e4m3xe5m2" : fmt == 3 ? "_e5m2" : "";
+}
+
 // The kernel a validated block-scaled problem runs on, and its workgroup count.
 const char *mx_kernel_name(int64_t M, int64_t N, int64_t K, bool packed)
 {
@@ -2789,11 +2804,42 @@ int64_t mx_tiles(int64_t M, int64_t N)
     return mx_uses_strip(M, N) ? mx_strip_tiles(M, N) : ((M + 255) / 256) * ((N + 255) / 256);
 }
 
+// The instantiations of the element encodings FMT (0..3).
+template <bool PK, int G>
+const void *mx_kernel_fn(int fmt)
+{
+    switch (fmt) {
+    case 1:
+        return reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, G, PK, 1>);
+    case 2:
+        return reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, G, PK, 2>);
+    case 3:
+        return reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, G, PK, 3>);
+    default:
+        return reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, G, PK, 0>);
+    }
+}
+template <bool PK>
+const void *mx_strip_fn(int fmt)
+{
+    switch (fmt) {
+    case 1:
+        return reinterpret_cast<const void *>(&gemm_mxf8_strip_kernel<TG_MX_STRIP_STAGES, PK, 1>);
+    case 2:
+        return reinterpret_cast<const void *>(&gemm_mxf8_strip_kernel<TG_MX_STRIP_STAGES, PK, 2>);
+    case 3:
+        return reinterpret_cast<const void *>(&gemm_mxf8_strip_kernel<TG_MX_STRIP_STAGES, PK, 3>);
+    default:
+        return reinterpret_cast<const void *>(&gemm_mxf8_strip_kernel<TG_MX_STRIP_STAGES, PK, 0>);
+    }
+}
+
 // Launch a validated, non-empty block-scaled problem; lds is the row stride
-// (row-major) or the 32-row group stride (packed) of each scale matrix.
+// (row-major) or the 32-row group stride (packed) of each scale matrix; fmt
+// the element encodings (FMT above).
 template <bool PK>
 int launch_mx(const void *A, const void *SA, const void *B, const void *SB, void *D, int64_t M, int64_t N,
-              int64_t K, int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd, void *stream)
+              int64_t K, int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd, int fmt, void *stream)
 {
     int st = check_device();
     if (st != TG_OK)
@@ -2807,9 +2853,8 @@ int launch_mx(const void *A, const void *SA, const void *B, const void *SB, void
         int stiles_n = (int)((N + 127) / 128);
         void *sargs[] = {(void *)&A, (void *)&SA, (void *)&B, (void *)&SB, (void *)&D, &Mi, &Ni, &Ki,
                          &lda, &ldsa, &ldb, &ldsb, &ldd, &stiles_n, &dvec};
-        hipError_t e =
-            hipLaunchKernel(reinterpret_cast<const void *>(&gemm_mxf8_strip_kernel<TG_MX_STRIP_STAGES, PK>),
-                            dim3((unsigned)sgrid), dim3(256), sargs, 0, (hipStream_t)stream);
+        hipError_t e = hipLaunchKernel(mx_strip_fn<PK>(fmt), dim3((unsigned)sgrid), dim3(256), sargs, 0,
+                                       (hipStream_t)stream);
         return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
     }
     int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
@@ -2820,16 +2865,16 @@ int launch_mx(const void *A, const void *SA, const void *B, const void *SB, void
                     &lda, &ldsa, &ldb, &ldsb, &ldd, &tiles_m, &tiles_n, &dvec};
     // groups of four K-tiles when they divide the K-tile count, else pairs
     // (at most one padding K-tile)
-    const void *fn = mx_group4(K) ? reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 4, PK>)
-                                 : reinterpret_cast<const void *>(&gemm_mxf8_kernel<256, 256, 2, 2, 2, PK>);
+    const void *fn = mx_group4(K) ? mx_kernel_fn<PK, 4>(fmt) : mx_kernel_fn<PK, 2>(fmt);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
-void mx_plan_out(const char *kernel, int64_t tiles, char *name, int64_t name_len, int64_t *tiles_out)
+void mx_plan_out(const char *kernel, int64_t tiles, char *name, int64_t name_len, int64_t *tiles_out,
+                 int fmt = 0)
 {
     if (name && name_len > 0)
-        snprintf(name, (size_t)name_len, "%s", kernel);
+        snprintf(name, (size_t)name_len, "%s%s", kernel, kernel[0] ? mx_fmt_suffix(fmt) : "");
     if (tiles_out)
         *tiles_out = tiles;
 }
@@ -2898,16 +2943,82 @@ extern "C" int tg_mx_pack_scales(const void *S, int64_t rows, int64_t K, int64_t
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
-extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const void *SB, void *D,
-                            int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb,
-                            int64_t ldsb, int64_t ldd, void *stream)
+// Element encodings of the block-scaled entry points: 0 E4M3, 1 E5M2.
+static int mx_fmt(int a_format, int b_format)
 {
+    if (a_format < 0 || a_format > 1 || b_format < 0 || b_format > 1)
+        return -1;
+    return a_format + 2 * b_format;
+}
+
+extern "C" int tg_gemm_mx(const void *A, const void *SA, const void *B, const void *SB, void *D, int64_t M,
+                          int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd,
+                          int a_format, int b_format, void *stream)
+{
+    const int fmt = mx_fmt(a_format, b_format);
+    if (fmt < 0)
+        return TG_ERR_INVALID_ARG;
     int st = validate_mx(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd);
     if (st != TG_OK)
         return st;
     if (M == 0 || N == 0)
         return TG_OK;
-    return launch_mx<false>(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd, stream);
+    return launch_mx<false>(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd, fmt, stream);
+}
+
+extern "C" int tg_gemm_mx_plan(const void *A, const void *SA, const void *B, const void *SB, const void *D,
+                               int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb,
+                               int64_t ldsb, int64_t ldd, int a_format, int b_format, char *name,
+                               int64_t name_len, int64_t *tiles)
+{
+    const int fmt = mx_fmt(a_format, b_format);
+    mx_plan_out("", 0, name, name_len, tiles);
+    if (fmt < 0)
+        return TG_ERR_INVALID_ARG;
+    int st = validate_mx(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd);
+    if (st != TG_OK || M == 0 || N == 0)
+        return st;
+    mx_plan_out(mx_kernel_name(M, N, K, false), mx_tiles(M, N), name, name_len, tiles, fmt);
+    return TG_OK;
+}
+
+extern "C" int tg_gemm_mx_packed(const void *A, const void *SA, const void *B, const void *SB, void *D, int64_t M,
+                                 int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd, int a_format,
+                                 int b_format, void *stream)
+{
+    const int fmt = mx_fmt(a_format, b_format);
+    if (fmt < 0)
+        return TG_ERR_INVALID_ARG;
+    int st = validate_mx_packed(A, SA, B, SB, D, M, N, K, lda, ldb, ldd);
+    if (st != TG_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    const int64_t stride = mx_packed_stride(K);
+    return launch_mx<true>(A, SA, B, SB, D, M, N, K, lda, stride, ldb, stride, ldd, fmt, stream);
+}
+
+extern "C" int tg_gemm_mx_packed_plan(const void *A, const void *SA, const void *B, const void *SB, const void *D,
+                                      int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
+                                      int a_format, int b_format, char *name, int64_t name_len, int64_t *tiles)
+{
+    const int fmt = mx_fmt(a_format, b_format);
+    mx_plan_out("", 0, name, name_len, tiles);
+    if (fmt < 0)
+        return TG_ERR_INVALID_ARG;
+    int st = validate_mx_packed(A, SA, B, SB, D, M, N, K, lda, ldb, ldd);
+    if (st != TG_OK || M == 0 || N == 0)
+        return st;
+    mx_plan_out(mx_kernel_name(M, N, K, true), mx_tiles(M, N), name, name_len, tiles, fmt);
+    return TG_OK;
+}
+
+// E4M3 on both operands
+extern "C" int tg_gemm_mxf8(const void *A, const void *SA, const void *B, const void *SB, void *D,
+                            int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldsa, int64_t ldb,
+                            int64_t ldsb, int64_t ldd, void *stream)
+{
+    return tg_gemm_mx(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd, 0, 0, stream);
 }
 
 extern "C" int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, const void *SB,
@@ -2915,37 +3026,21 @@ extern "C" int tg_gemm_mxf8_plan(const void *A, const void *SA, const void *B, c
                                  int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd, char *name,
                                  int64_t name_len, int64_t *tiles)
 {
-    int st = validate_mx(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd);
-    mx_plan_out("", 0, name, name_len, tiles);
-    if (st != TG_OK || M == 0 || N == 0)
-        return st;
-    mx_plan_out(mx_kernel_name(M, N, K, false), mx_tiles(M, N), name, name_len, tiles);
-    return TG_OK;
+    return tg_gemm_mx_plan(A, SA, B, SB, D, M, N, K, lda, ldsa, ldb, ldsb, ldd, 0, 0, name, name_len, tiles);
 }
 
 extern "C" int tg_gemm_mxf8_packed(const void *A, const void *SA, const void *B, const void *SB, void *D,
                                    int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
                                    void *stream)
 {
-    int st = validate_mx_packed(A, SA, B, SB, D, M, N, K, lda, ldb, ldd);
-    if (st != TG_OK)
-        return st;
-    if (M == 0 || N == 0)
-        return TG_OK;
-    const int64_t stride = mx_packed_stride(K);
-    return launch_mx<true>(A, SA, B, SB, D, M, N, K, lda, stride, ldb, stride, ldd, stream);
+    return tg_gemm_mx_packed(A, SA, B, SB, D, M, N, K, lda, ldb, ldd, 0, 0, stream);
 }
 
 extern "C" int tg_gemm_mxf8_packed_plan(const void *A, const void *SA, const void *B, const void *SB,
                                         const void *D, int64_t M, int64_t N, int64_t K, int64_t lda,
                                         int64_t ldb, int64_t ldd, char *name, int64_t name_len, int64_t *tiles)
 {
-    int st = validate_mx_packed(A, SA, B, SB, D, M, N, K, lda, ldb, ldd);
-    mx_plan_out("", 0, name, name_len, tiles);
-    if (st != TG_OK || M == 0 || N == 0)
-        return st;
-    mx_plan_out(mx_kernel_name(M, N, K, true), mx_tiles(M, N), name, name_len, tiles);
-    return TG_OK;
+    return tg_gemm_mx_packed_plan(A, SA, B, SB, D, M, N, K, lda, ldb, ldd, 0, 0, name, name_len, tiles);
 }
 
 extern "C" int tg_device_info(int *compute_units, int *max_clock_khz, char *arch, int64_t arch_len)

@@ -225,6 +225,47 @@ int tg_gemm_mxf8_packed_plan(const void *A, const void *SA, const void *B, const
                              int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
                              char *name, int64_t name_len, int64_t *tiles);
 
+/*
+ * Element encodings of the block-scaled GEMM.  OCP MX defines two FP8
+ * element encodings; tg_gemm_mxf8 and tg_gemm_mxf8_packed take E4M3 on both
+ * operands, tg_gemm_mx and tg_gemm_mx_packed take either on each:
+ *   TG_MX_E4M3  sign, 4 exponent bits (bias 7), 3 fraction bits; no
+ *               infinities, S.1111.111 is NaN, largest finite 448.
+ *   TG_MX_E5M2  sign, 5 exponent bits (bias 15), 2 fraction bits; exponent
+ *               31 is ±infinity (fraction 0) or NaN, largest finite 57344
+ *               (the upper byte of a binary16 pattern).
+ * Infinite or NaN elements and scales propagate through the fp32 sum as IEEE
+ * arithmetic has them (infinity times zero is NaN); a result past binary16's
+ * range is ±infinity.
+ */
+enum { TG_MX_E4M3 = 0, TG_MX_E5M2 = 1 };
+
+/*
+ * tg_gemm_mx — tg_gemm_mxf8 with the element encoding of A (a_format) and of
+ * B (b_format) chosen separately among TG_MX_E4M3 and TG_MX_E5M2 (the same
+ * scale bytes, layouts, kernels and status codes; any other format value is
+ * TG_ERR_INVALID_ARG).  tg_gemm_mx with both formats TG_MX_E4M3 is
+ * tg_gemm_mxf8.  tg_gemm_mx_plan, tg_gemm_mx_packed and
+ * tg_gemm_mx_packed_plan extend tg_gemm_mxf8_plan, tg_gemm_mxf8_packed and
+ * tg_gemm_mxf8_packed_plan the same way; a plan's kernel name carries the
+ * encodings as a suffix ("_e5m2" for both E5M2, "_e5m2xe4m3" for A E5M2 and
+ * B E4M3, "_e4m3xe5m2" for the reverse; none for E4M3 on both).
+ */
+int tg_gemm_mx(const void *A, const void *SA, const void *B, const void *SB, void *D,
+               int64_t M, int64_t N, int64_t K,
+               int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd,
+               int a_format, int b_format, void *stream);
+int tg_gemm_mx_plan(const void *A, const void *SA, const void *B, const void *SB, const void *D,
+                    int64_t M, int64_t N, int64_t K,
+                    int64_t lda, int64_t ldsa, int64_t ldb, int64_t ldsb, int64_t ldd,
+                    int a_format, int b_format, char *name, int64_t name_len, int64_t *tiles);
+int tg_gemm_mx_packed(const void *A, const void *SA, const void *B, const void *SB, void *D,
+                      int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
+                      int a_format, int b_format, void *stream);
+int tg_gemm_mx_packed_plan(const void *A, const void *SA, const void *B, const void *SB, const void *D,
+                           int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldd,
+                           int a_format, int b_format, char *name, int64_t name_len, int64_t *tiles);
+
 /* tg_status_string — a static, NUL-terminated description of a status. */
 const char *tg_status_string(int status);
 

@@ -97,12 +97,14 @@ def pack_scales(S, rows, K, lds):
     return P
 
 
-def run_mx(a, sa, b, sb, M, N, K, guard=0, label="", packed=False):
+def run_mx(a, sa, b, sb, M, N, K, guard=0, label="", packed=False, a_fmt=0, b_fmt=0):
     """D (M, N) fp16 window and the full (M+2g, N+2g) buffer (uint16) of
     tg_gemm_mxf8 on byte arrays a (M, lda), sa (M, ldsa), b (N, ldb), sb
     (N, ldsb); every byte in them is passed to the device as is.  With
     packed=True the scales are first converted on the device into the packed
-    layout (tg_mx_pack_scales) and tg_gemm_mxf8_packed runs instead."""
+    layout (tg_mx_pack_scales) and tg_gemm_mxf8_packed runs instead.  Element
+    encodings other than E4M3 on both operands (a_fmt, b_fmt: 0 E4M3, 1 E5M2)
+    go through tg_gemm_mx / tg_gemm_mx_packed."""
     import torch
 
     import dense_fp16_gemm_02_amd as tg
@@ -113,12 +115,18 @@ def run_mx(a, sa, b, sb, M, N, K, guard=0, label="", packed=False):
     d = torch.full(((M + 2 * guard) * ldd + 8,), SENTINEL, dtype=torch.int16, device="cuda:0")
     dptr = d.data_ptr() + 2 * (guard * ldd + guard)
     say(f"mxf8 {label} M={M} N={N} K={K} lda={lda} ldsa={ldsa} ldb={ldb} ldsb={ldsb} guard={guard} "
-        f"packed={packed}")
+        f"packed={packed} formats=({a_fmt},{b_fmt})")
+    s = torch.cuda.current_stream()
     if packed:
         PA, PB = pack_scales(SA, M, K, ldsa), pack_scales(SB, N, K, ldsb)
-        st = tg.tg_gemm_mxf8_packed(A, PA, B, PB, dptr, M, N, K, lda, ldb, ldd, torch.cuda.current_stream())
+        if a_fmt or b_fmt:
+            st = tg.tg_gemm_mx_packed(A, PA, B, PB, dptr, M, N, K, lda, ldb, ldd, a_fmt, b_fmt, s)
+        else:
+            st = tg.tg_gemm_mxf8_packed(A, PA, B, PB, dptr, M, N, K, lda, ldb, ldd, s)
+    elif a_fmt or b_fmt:
+        st = tg.tg_gemm_mx(A, SA, B, SB, dptr, M, N, K, lda, ldsa, ldb, ldsb, ldd, a_fmt, b_fmt, s)
     else:
-        st = tg.tg_gemm_mxf8(A, SA, B, SB, dptr, M, N, K, lda, ldsa, ldb, ldsb, ldd, torch.cuda.current_stream())
+        st = tg.tg_gemm_mxf8(A, SA, B, SB, dptr, M, N, K, lda, ldsa, ldb, ldsb, ldd, s)
     torch.cuda.synchronize()
     full = d.cpu().numpy().view(np.uint16)[:(M + 2 * guard) * ldd].reshape(M + 2 * guard, ldd)
     win = np.array(full[guard:guard + M, guard:guard + N].view(np.float16))

@@ -87,6 +87,15 @@ MX_CASES: dict[str, Case] = {
 # the same kernels reading scales in the packed layout (tg_gemm_mxf8_packed)
 MXP_CASES: dict[str, Case] = {n.replace("gemm_mxf8_", "gemm_mxf8p_"): c for n, c in MX_CASES.items()}
 
+# the other element encodings (tg_gemm_mx, tg_gemm_mx_packed): (A, B) encodings
+# (0 E4M3, 1 E5M2) and the name suffix they add
+MX_FMT_SUFFIX = {(1, 0): "_e5m2xe4m3", (0, 1): "_e4m3xe5m2", (1, 1): "_e5m2"}
+MXF_CASES: dict[str, tuple] = {
+    n + sfx: (c, fa, fb, n in MXP_CASES)
+    for n, c in list(MX_CASES.items()) + list(MXP_CASES.items())
+    for (fa, fb), sfx in MX_FMT_SUFFIX.items()
+}
+
 TILES = sorted({t for t, _ in _F16_BF16})
 PATHS = ("dma", "vec", "scalar")
 DMA_ONLY = {"256x256_w2x2_pers", "128x128_w2x2_ws"}  # kernels only on the direct-to-LDS path

@@ -19,7 +19,7 @@ import pytest
 import oracle
 import workloads
 from gpu_util import NAN_BITS, SENTINEL, run_mx, say
-from planner_cases import CASES, MX_CASES, MXP_CASES
+from planner_cases import CASES, MX_CASES, MXF_CASES, MXP_CASES
 
 torch = pytest.importorskip("torch")
 tg = pytest.importorskip("dense_fp16_gemm_02_amd")
@@ -106,4 +106,36 @@ def test_mx_instantiation_exact(name):
     d, _, st = run_mx(a, sa, b, sb, M, N, K, label=f"coverage {name}", packed=packed)
     assert st == tg.TG_OK
     res = oracle.gemm_mx(a, sa, b, sb, M, N, K)
+    assert np.array_equal(d.view(np.uint16), res.d.view(np.uint16))
+
+
+# +1, -1, 0 in each element encoding (E4M3, E5M2)
+UNIT_CODES = {0: (0x38, 0xb8, 0x00), 1: (0x3c, 0xbc, 0x00)}
+
+
+@pytest.mark.parametrize("name", sorted(MXF_CASES))
+def test_mx_format_instantiation_exact(name):
+    """Every instantiation of the other element encodings, on {-1, 0, 1}
+    elements with random power-of-two scales: D equals the oracle bit for
+    bit (every partial sum is exact in fp32)."""
+    c, fa, fb, packed = MXF_CASES[name]
+    M, N, K = c.M, c.N, c.K
+    rng = np.random.default_rng(K + M + 7 * fa + 13 * fb)
+    a = rng.choice(np.array(UNIT_CODES[fa], np.uint8), size=(M, K))
+    b = rng.choice(np.array(UNIT_CODES[fb], np.uint8), size=(N, K))
+    nb = K // 32
+    ld = max(4, (nb + 3) // 4 * 4)
+    sa = workloads.pad_bytes(rng.integers(124, 131, size=(M, nb)).astype(np.uint8), ld, 0xff)
+    sb = workloads.pad_bytes(rng.integers(124, 131, size=(N, nb)).astype(np.uint8), ld, 0xff)
+    if packed:
+        st, planned, _ = tg.tg_gemm_mx_packed_plan(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+                                                   M, N, K, K, K, N, fa, fb)
+    else:
+        st, planned, _ = tg.tg_gemm_mx_plan(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+                                            M, N, K, K, ld, K, ld, N, fa, fb)
+    assert st == tg.TG_OK and planned == name, (planned, name)
+    d, _, st = run_mx(a, sa, b, sb, M, N, K, label=f"coverage {name}", packed=packed, a_fmt=fa, b_fmt=fb)
+    assert st == tg.TG_OK
+    fmts = ("e4m3", "e5m2")
+    res = oracle.gemm_mx(a, sa, b, sb, M, N, K, a_fmt=fmts[fa], b_fmt=fmts[fb])
     assert np.array_equal(d.view(np.uint16), res.d.view(np.uint16))

@@ -164,3 +164,18 @@ def test_unknown_encoding_is_refused(oracle_lib):
     s = np.full((1, 1), 127, np.uint8)
     with pytest.raises(ValueError):
         oracle.gemm_mx(a, s, a, s, 1, 1, 32, a_fmt="e3m4")
+
+
+def test_e5m2_input_encoder(oracle_lib):
+    """The input encoder (workloads, not the oracle) maps every finite E5M2
+    value to its own code and keeps every element of a block within the
+    encoding's relative spacing of the block's largest element."""
+    vals = oracle.e5m2_to_double(np.arange(0x7c, dtype=np.uint8))
+    assert np.array_equal(workloads.encode_e5m2(vals), np.arange(0x7c, dtype=np.uint8))
+    assert np.array_equal(workloads.encode_e5m2(-vals[1:]), (np.arange(1, 0x7c) | 0x80).astype(np.uint8))
+    x = np.random.default_rng(8).normal(size=(6, 100))
+    codes, scales = workloads.mx_quantize(x, "e5m2")
+    v = oracle.e5m2_to_double(codes) * np.repeat(oracle.e8m0_to_double(scales), 32, axis=1)[:, :100]
+    amax = np.repeat(np.array([[np.abs(x[r, b:b + 32]).max() for b in range(0, 100, 32)] for r in range(6)]),
+                     32, axis=1)[:, :100]
+    assert np.all(np.abs(v - x) <= amax * 2.0 ** -2)

@@ -12,7 +12,7 @@ import itertools
 
 import pytest
 
-from planner_cases import CASES, MX_CASES, MXP_CASES, all_fp_names, vec_lda
+from planner_cases import CASES, MX_CASES, MX_FMT_SUFFIX, MXF_CASES, MXP_CASES, all_fp_names, vec_lda
 
 tg = pytest.importorskip("dense_fp16_gemm_02_amd")
 
@@ -73,6 +73,40 @@ def test_mx_planner_sweep_stays_inside_the_table():
         assert st == tg.TG_OK and pname == name.replace("gemm_mxf8_", "gemm_mxf8p_"), (M, N, K, pname)
         seen.add(pname)
     assert seen == set(MX_CASES) | set(MXP_CASES)
+
+
+def test_format_cases_plan_to_their_names():
+    """tg_gemm_mx(_packed)_plan: the kernel of the E4M3 plan with the
+    encodings' suffix; E4M3 on both operands is exactly tg_gemm_mxf8's plan."""
+    for name, (c, fa, fb, packed) in MXF_CASES.items():
+        nb = c.K // 32
+        ld = max(4, (nb + 3) // 4 * 4)
+        if packed:
+            st, got, tiles = tg.tg_gemm_mx_packed_plan(BASE, BASE, BASE, BASE, BASE, c.M, c.N, c.K, c.K, c.K,
+                                                       c.N, fa, fb)
+        else:
+            st, got, tiles = tg.tg_gemm_mx_plan(BASE, BASE, BASE, BASE, BASE, c.M, c.N, c.K, c.K, ld, c.K, ld,
+                                                c.N, fa, fb)
+        assert st == tg.TG_OK and got == name and tiles > 0, (name, got)
+    for name, c in MX_CASES.items():
+        nb = c.K // 32
+        ld = max(4, (nb + 3) // 4 * 4)
+        assert tg.tg_gemm_mx_plan(BASE, BASE, BASE, BASE, BASE, c.M, c.N, c.K, c.K, ld, c.K, ld, c.N, 0, 0) == \
+            tg.tg_gemm_mxf8_plan(BASE, BASE, BASE, BASE, BASE, c.M, c.N, c.K, c.K, ld, c.K, ld, c.N)
+    assert len(MXF_CASES) == len(MX_FMT_SUFFIX) * (len(MX_CASES) + len(MXP_CASES))
+
+
+@pytest.mark.parametrize("fa,fb", [(2, 0), (0, 2), (-1, 0), (0, -1), (7, 7)])
+def test_unknown_encodings_are_refused(fa, fb):
+    st, name, tiles = tg.tg_gemm_mx_plan(BASE, BASE, BASE, BASE, BASE, 64, 64, 64, 64, 4, 64, 4, 64, fa, fb)
+    assert st == tg.TG_ERR_INVALID_ARG and name == "" and tiles == 0
+    st, name, tiles = tg.tg_gemm_mx_packed_plan(BASE, BASE, BASE, BASE, BASE, 64, 64, 64, 64, 64, 64, fa, fb)
+    assert st == tg.TG_ERR_INVALID_ARG and name == "" and tiles == 0
+    # refused before the device is touched (this runs without a GPU)
+    assert tg.tg_gemm_mx(BASE, BASE, BASE, BASE, BASE, 64, 64, 64, 64, 4, 64, 4, 64, fa, fb, None) == \
+        tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_mx_packed(BASE, BASE, BASE, BASE, BASE, 64, 64, 64, 64, 64, 64, fa, fb, None) == \
+        tg.TG_ERR_INVALID_ARG
 
 
 def test_persistent_kernel_conditions():

@@ -188,7 +188,10 @@ def small_int_pattern(M: int, N: int, K: int, dtype: str = "f16"):
 # exponent; 448 = 1.75·2^8), clamped to [-127, 127] (an all-zero block takes
 # -127), and every element x / 2^exp is rounded to the nearest E4M3 value,
 # ties to the even code, saturating at ±448.  This is input preparation only:
-# the GEMM consumes the codes and scales as given.
+# the GEMM consumes the codes and scales as given.  E5M2 operands (OCP MX's
+# second FP8 encoding) are encoded the same way with the shared exponent
+# floor(log2(max |x|)) minus 15 (57344 = 1.75·2^15) and saturation at
+# ±57344.
 
 MX_BLOCK = 32
 MX_NAN = np.uint8(0x7f)
@@ -205,6 +208,33 @@ def _e4m3_grid():
 _E4M3_VALS, _E4M3_CODES = _e4m3_grid()
 
 
+def _e5m2_grid():
+    """The 124 non-negative finite E5M2 values in code order (increasing)."""
+    codes = np.arange(0x7c, dtype=np.int64)
+    e, f = codes >> 2, codes & 3
+    vals = np.where(e == 0, f * 2.0 ** -16, (4 + f) * 2.0 ** (e - 17))
+    return vals, codes.astype(np.uint8)
+
+
+_E5M2_VALS, _E5M2_CODES = _e5m2_grid()
+
+
+def _encode_grid(q, vals, codes, top, top_code):
+    q = np.asarray(q, dtype=np.float64)
+    a = np.minimum(np.abs(q), top)
+    i = np.clip(np.searchsorted(vals, a, side="right") - 1, 0, len(vals) - 2)
+    lo, hi = vals[i], vals[i + 1]
+    up = (hi - a < a - lo) | ((hi - a == a - lo) & ((codes[i] & 1) == 1))
+    c = np.where(up, codes[i + 1], codes[i]).astype(np.uint8)
+    c = np.where(a >= top, np.uint8(top_code), c)
+    return np.where((q < 0) & (c != 0), c | np.uint8(0x80), c).astype(np.uint8)
+
+
+def encode_e5m2(q: np.ndarray) -> np.ndarray:
+    """Nearest E5M2 code (ties to the even code), saturating at ±57344."""
+    return _encode_grid(q, _E5M2_VALS, _E5M2_CODES, 57344.0, 0x7b)
+
+
 def encode_e4m3(q: np.ndarray) -> np.ndarray:
     """Nearest E4M3 code (ties to the even code), saturating at ±448."""
     q = np.asarray(q, dtype=np.float64)
@@ -217,9 +247,13 @@ def encode_e4m3(q: np.ndarray) -> np.ndarray:
     return np.where((q < 0) & (c != 0), c | np.uint8(0x80), c).astype(np.uint8)
 
 
-def mx_quantize(x: np.ndarray):
+def mx_quantize(x: np.ndarray, fmt: str = "e4m3"):
     """Encode a float64 (rows, K) matrix as (codes (rows, K) uint8, scales
-    (rows, ceil(K/32)) uint8) with the shared-exponent recipe above."""
+    (rows, ceil(K/32)) uint8) with the shared-exponent recipe above, in the
+    element encoding ``fmt`` ("e4m3" or "e5m2")."""
+    if fmt not in ("e4m3", "e5m2"):
+        raise ValueError("fmt is 'e4m3' or 'e5m2'")
+    top_exp = 8 if fmt == "e4m3" else 15
     x = np.asarray(x, dtype=np.float64)
     rows, K = x.shape
     nb = (K + MX_BLOCK - 1) // MX_BLOCK
@@ -228,20 +262,22 @@ def mx_quantize(x: np.ndarray):
     blocks = padded.reshape(rows, nb, MX_BLOCK)
     amax = np.abs(blocks).max(axis=2)
     with np.errstate(divide="ignore"):
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - top_exp, -127)
     e = np.clip(e, -127, 127).astype(np.int64)
-    codes = encode_e4m3(blocks / np.exp2(e)[:, :, None]).reshape(rows, nb * MX_BLOCK)[:, :K]
+    enc = encode_e4m3 if fmt == "e4m3" else encode_e5m2
+    codes = enc(blocks / np.exp2(e)[:, :, None]).reshape(rows, nb * MX_BLOCK)[:, :K]
     return np.ascontiguousarray(codes), (e + 127).astype(np.uint8)
 
 
-def make_mx_inputs(w: Workload):
+def make_mx_inputs(w: Workload, a_fmt: str = "e4m3", b_fmt: str = "e4m3"):
     """Block-scaled FP8 operands for workload ``w``: (A, SA, B, SB), the same
-    float64 draws as ``make_inputs`` encoded with ``mx_quantize``."""
+    float64 draws as ``make_inputs`` encoded with ``mx_quantize`` (element
+    encodings a_fmt, b_fmt)."""
     a = _draw64(np.random.Generator(np.random.PCG64(SEED_A_BASE + w.index)), (w.M, w.K), w.dist_a)
     b = _draw64(np.random.Generator(np.random.PCG64(SEED_B_BASE + w.index)), (w.N, w.K), w.dist_b)
-    qa, sa = mx_quantize(a)
+    qa, sa = mx_quantize(a, a_fmt)
     del a
-    qb, sb = mx_quantize(b)
+    qb, sb = mx_quantize(b, b_fmt)
     return qa, sa, qb, sb
 
 
