@@ -226,8 +226,10 @@ int tg_gemm_mxf8_packed_plan(const void *A, const void *SA, const void *B, const
                              char *name, int64_t name_len, int64_t *tiles);
 
 /*
- * Element encodings of the block-scaled GEMM.  OCP MX defines two FP8
- * element encodings; tg_gemm_mxf8 and tg_gemm_mxf8_packed take E4M3 on both
+ * Element encodings of the block-scaled GEMM.  The pages name the
+ * block-scaled FP8 GEMM ("TIRx Layout API", section "Scale Factor 布局")
+ * without fixing its element encoding; OCP MX defines two FP8 element
+ * encodings; tg_gemm_mxf8 and tg_gemm_mxf8_packed take E4M3 on both
  * operands, tg_gemm_mx and tg_gemm_mx_packed take either on each:
  *   TG_MX_E4M3  sign, 4 exponent bits (bias 7), 3 fraction bits; no
  *               infinities, S.1111.111 is NaN, largest finite 448.
