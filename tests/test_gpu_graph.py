@@ -4,7 +4,8 @@ HIP graph and replayed.  Each case captures one call on a side stream,
 replays the graph several times with eager work and synchronizations
 between the replays, and requires every replay's D to equal the eager
 call's D bit for bit; the fp16 cases' operands are small integers, so D is
-also compared with the oracle bit for bit."""
+also compared with the oracle bit for bit, and the block-scaled case with
+E5M2 and E4M3 operands is compared with the oracle within its tolerance."""
 import numpy as np
 import pytest
 
@@ -83,3 +84,25 @@ def test_block_scaled_packed_call_replays_in_a_graph():
                            torch.cuda.current_stream()) == tg.TG_OK
     torch.cuda.synchronize()
     assert torch.equal(want.view(torch.int16), D2.view(torch.int16))
+
+
+def test_block_scaled_mixed_encodings_replay_in_a_graph():
+    # E5M2 elements in A, E4M3 in B, through tg_gemm_mx_packed; the E5M2
+    # scales sit lower so that every sum stays inside binary16's range
+    M, N, K = 2100, 2060, 512
+    qa, sa = workloads.random_mx(63, M, K, 112, 115, fmt="e5m2")
+    qb, sb = workloads.random_mx(64, N, K, 120, 126)
+    A, SA, B, SB = _bytes(qa), _bytes(sa), _bytes(qb), _bytes(sb)
+    PA, PB = pack_scales(SA, M, K, sa.shape[1]), pack_scales(SB, N, K, sb.shape[1])
+    D = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    want = _replays_match(
+        lambda s: tg.tg_gemm_mx_packed(A, PA, B, PB, D, M, N, K, K, K, N, tg.TG_MX_E5M2, tg.TG_MX_E4M3, s), D,
+        "mx packed e5m2 x e4m3")
+    D2 = torch.empty_like(D)
+    assert tg.tg_gemm_mx(A, SA, B, SB, D2, M, N, K, K, sa.shape[1], K, sb.shape[1], N, tg.TG_MX_E5M2,
+                         tg.TG_MX_E4M3, torch.cuda.current_stream()) == tg.TG_OK
+    torch.cuda.synchronize()
+    assert torch.equal(want.view(torch.int16), D2.view(torch.int16))
+    res = oracle.gemm_mx(qa, sa, qb, sb, M, N, K, a_fmt="e5m2", b_fmt="e4m3")
+    ok, _, report = oracle.check(want.cpu().numpy(), res)
+    assert ok, report

@@ -9,9 +9,10 @@ instantiation once; here the shapes and strides are arbitrary.  Half of
 the fp16 and bf16 cases use {-1, 0, 1} operands, where D must equal the
 oracle bit for bit; the others use N(0,1) data checked with the oracle's
 tolerance on every element.  Operand padding holds NaN, and the guard band
-around D must be untouched.  The block-scaled cases draw random E4M3 codes
-and scales (both scale layouts).  Each case prints its parameters before it
-runs."""
+around D must be untouched.  The block-scaled cases draw random codes and
+scales (both scale layouts) with the element encoding of each operand drawn
+too: E4M3 on both through tg_gemm_mxf8, otherwise E4M3 or E5M2 per operand
+through tg_gemm_mx.  Each case prints its parameters before it runs."""
 import numpy as np
 import pytest
 
@@ -96,8 +97,14 @@ def test_random_block_scaled_problem(seed, packed):
     M = int(rng.integers(1, 2300 if big else 300))
     N = int(rng.integers(1, 2300 if big else 300))
     K = 32 * int(rng.integers(1, 20))
-    qa, sa = workloads.random_mx(9600 + seed, M, K, 118, 124)
-    qb, sb = workloads.random_mx(9700 + seed, N, K, 118, 124)
+    # element encodings from a stream of their own, so the shapes stay those
+    # of E4M3 on both; E5M2 reaches 57344, so its scales sit lower (no sum
+    # leaves binary16's range)
+    fa, fb = (int(x) for x in np.random.default_rng(9800 + seed).integers(0, 2, size=2))
+    fmts = ("e4m3", "e5m2")
+    lo_hi = ((118, 124), (111, 115))
+    qa, sa = workloads.random_mx(9600 + seed, M, K, *lo_hi[fa], fmt=fmts[fa])
+    qb, sb = workloads.random_mx(9700 + seed, N, K, *lo_hi[fb], fmt=fmts[fb])
     nb = K // 32
     ld_s = max(4, (nb + 3) // 4 * 4) + 4 * int(rng.integers(0, 2))
     a = workloads.pad_bytes(qa, K + 16 * int(rng.integers(0, 3)))
@@ -105,9 +112,10 @@ def test_random_block_scaled_problem(seed, packed):
     sa_p = workloads.pad_bytes(sa, ld_s, 0xff)
     sb_p = workloads.pad_bytes(sb, ld_s, 0xff)
     guard = int(rng.integers(0, 3))
-    label = f"random mxf8 seed={seed} packed={packed} {M}x{N}x{K}"
-    res = oracle.gemm_mx(qa, sa, qb, sb, M, N, K)
-    d, full, st = run_mx(a, sa_p, b, sb_p, M, N, K, guard=guard, label=label, packed=packed)
+    label = f"random block-scaled seed={seed} packed={packed} {M}x{N}x{K} formats=({fmts[fa]},{fmts[fb]})"
+    res = oracle.gemm_mx(qa, sa, qb, sb, M, N, K, a_fmt=fmts[fa], b_fmt=fmts[fb])
+    d, full, st = run_mx(a, sa_p, b, sb_p, M, N, K, guard=guard, label=label, packed=packed,
+                         a_fmt=fa, b_fmt=fb)
     assert st == tg.TG_OK
     mask = np.ones(full.shape, bool)
     mask[guard:guard + M, guard:guard + N] = False
