@@ -106,3 +106,26 @@ def test_sum_past_binary16_range_is_infinity():
     d, _, st = run_mx(a, s[:M], b, s[:N], M, N, K, label="e5m2 overflow", a_fmt=1, b_fmt=1)
     assert st == tg.TG_OK
     assert np.all(d[:, [0, 1, 6]] == np.inf) and np.all(d[:, 5] == 57344.0)
+
+
+# E5M2 on both operands for every large workload; the mixed pair on the
+# linear shape only (same kernel, other format fields)
+LARGE_CASES = [(w, 1, 1) for w in workloads.WORKLOADS if w.M * w.N * w.K > 2 ** 31] + \
+    [(workloads.BY_NAME["linear_8192x14336x4096"], 1, 0)]
+
+
+@pytest.mark.parametrize("w,fa,fb", LARGE_CASES,
+                         ids=lambda v: v.name if hasattr(v, "name") else FMTS[v])
+def test_large_workloads_sampled_rows(w, fa, fb):
+    """The benchmark's inputs and launch (packed scales, the kernel the plan
+    picks) with E5M2 elements: the seeded draws encoded per block, D's
+    sampled rows against the oracle on every column, the rest finite."""
+    qa, sa, qb, sb = workloads.make_mx_inputs(w, FMTS[fa], FMTS[fb])
+    rows = workloads.sample_rows(w)
+    res = oracle.gemm_mx(qa, sa, qb, sb, w.M, w.N, w.K, rows=rows, a_fmt=FMTS[fa], b_fmt=FMTS[fb])
+    label = f"{w.name} formats=({FMTS[fa]},{FMTS[fb]}) sampled rows"
+    d, _, st = run_mx(qa, sa, qb, sb, w.M, w.N, w.K, label=label, packed=True, a_fmt=fa, b_fmt=fb)
+    assert st == tg.TG_OK
+    ok, worst, report = oracle.check(d[rows], res)
+    assert ok, f"{label}: {report}"
+    assert np.all(np.isfinite(d.astype(np.float32)))
