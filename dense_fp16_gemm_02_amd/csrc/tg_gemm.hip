@@ -2125,7 +2125,9 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_mxf8_ke
 // rows 0..63 and 64..127) fills one of three scale slots (scattered scale
 // loads cost the address unit per cache line: a DMA per K-tile cost 18% of
 // the time); at the other K-tiles, and always in wave 3, an empty DMA into
-// a spare slot keeps every wave's count of DMAs in flight the same.  B's
+// a spare slot keeps every wave's count of DMAs in flight the same; each
+// lane copies its fragment rows' four words into registers at the group's
+// first K-tile and picks the K-tile's word from them after that.  B's
 // DMAs stream past the caches; the workgroups on XCD x start their K loop at
 // K-tile x·KT/8 (rounded down to a group) and wrap around, so the eight XCDs
 // read different column bands of B's rows at a time.  Each K-tile: wait for
@@ -2250,6 +2252,16 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
             for (int v = 0; v < 16; ++v)
                 acc[i][j][v] = 0.0f;
 
+    // the scale words of the current group of four K-tiles: the four words of
+    // each of the lane's fragment rows (row r's words sit at bytes 16·r ..
+    // 16·r+15 of the slot, B's rows after A's 64), read from LDS once, at the
+    // group's first K-tile — each lane reads its row's whole 16 bytes, so
+    // sixteen consecutive rows fill all 64 banks once — and kept in
+    // registers for the group's other K-tiles, whose scale selection then
+    // waits on no LDS read
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 ga[TM], gb[TN];
+
 #pragma unroll
     for (int t = 0; t < STAGES - 1; ++t)
         issue(t);
@@ -2258,33 +2270,37 @@ __global__ __launch_bounds__(256) void gemm_mxf8_strip_kernel(
         barrier_lds();                    // ... every wave's; the stage of t-1 is drained
         issue(t + STAGES - 1);
         const uint8_t *st = smem + (t % STAGES) * STAGE;
+        // a group starts at every K-tile that is a multiple of four (the loop
+        // starts at one and wraps around to K-tile 0); its words landed with
+        // this K-tile's DMAs
+        const int kt = ktile(t);
+        if (kt % 4 == 0) {
+            const u32x4 *sw = reinterpret_cast<const u32x4 *>(sc_ring + slot(t) * SC_SLOT);
+#pragma unroll
+            for (int q = 0; q < TM; ++q)
+                ga[q] = sw[q * 32 + srow];
+#pragma unroll
+            for (int q = 0; q < TN; ++q)
+                gb[q] = sw[64 + wave * WTN + q * 32 + srow];
+        }
         // scale words: blocks at or past K/32 become 2^0 (the operand bytes
         // there are zero, the padding's scale bytes may be anything); lane
-        // r + 32·h shifts by 8·h so that byte 2·kk holds block 4·kt + 2·kk + h
-        const int nv = nblk - 4 * ktile(t);
+        // r + 32·h shifts by 8·h so that byte 2·kk holds block 4·kt + 2·kk + h;
+        // word kt mod 4 of the group's four is a wave-uniform choice
+        const int nv = nblk - 4 * kt;
         const uint32_t keep = nv >= 4 ? 0xffffffffu : (1u << (8 * nv)) - 1u;
         const uint32_t unit = 0x7f7f7f7fu & ~keep;
-        // the four words of row r sit at bytes 16·r .. 16·r+15 of the slot
-        // (B's rows after A's 64); each lane reads its row's whole 16 bytes
-        // — sixteen consecutive rows fill all 64 banks once, where 4-byte
-        // reads 16 bytes apart put two rows on every bank — and keeps word
-        // kt mod 4 (a wave-uniform choice)
-        // (the empty asm keeps the compiler from narrowing the read back to
-        // the one word used)
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 *sw = reinterpret_cast<const u32x4 *>(sc_ring + slot(t) * SC_SLOT);
-        const int wsel = ktile(t) % 4;
-        auto pick = [wsel](u32x4 v) {
-            asm volatile("" : "+v"(v));
+        const int wsel = kt % 4;
+        auto pick = [wsel](const u32x4 &v) {
             return wsel == 0 ? v[0] : wsel == 1 ? v[1] : wsel == 2 ? v[2] : v[3];
         };
         uint32_t wa[TM], wb[TN];
 #pragma unroll
         for (int q = 0; q < TM; ++q)
-            wa[q] = ((pick(sw[q * 32 + srow]) & keep) | unit) >> (8 * shalf);
+            wa[q] = ((pick(ga[q]) & keep) | unit) >> (8 * shalf);
 #pragma unroll
         for (int q = 0; q < TN; ++q)
-            wb[q] = ((pick(sw[64 + wave * WTN + q * 32 + srow]) & keep) | unit) >> (8 * shalf);
+            wb[q] = ((pick(gb[q]) & keep) | unit) >> (8 * shalf);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             i32x8 fa[TM], fb[TN];
