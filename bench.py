@@ -498,6 +498,80 @@ def hbm_ceiling(args, nbytes: int = 1 << 30) -> int:
     return 0
 
 
+def xcd_times(w, args) -> int:
+    """W untimed calls of tg_gemm_f16, then K calls through its stamping form
+    (tg_gemm_f16_xcd_stamps: the persistent kernel recording each
+    workgroup's start, end and XCD), each into its own slice of one stamps
+    buffer, with no synchronization between the calls.  Per call, each XCD's
+    end is its last workgroup's end, measured from the call's first start on
+    the constant 100 MHz clock; the launch ends with the slowest XCD.  Prints
+    one JSON line: per-XCD mean ends, the mean span, and the share of the span
+    after the mean XCD end (the time one XCD finishing late costs)."""
+    import numpy as np
+    import torch
+
+    import dense_fp16_gemm_02_amd as tg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    a, b = workloads.make_inputs(w)
+    A0 = torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16)
+    B0 = torch.from_numpy(b.view(np.int16)).to(dev).view(torch.float16)
+    sets = [(A0 if r == 0 else A0.clone(), B0 if r == 0 else B0.clone(),
+             torch.empty((w.M, w.N), dtype=torch.float16, device=dev)) for r in range(2)]
+    stream = torch.cuda.current_stream(dev)
+    st, kname, tiles = tg.tg_gemm_f16_plan(A0, B0, sets[0][2], w.M, w.N, w.K, w.K, w.K, w.N)
+    if st != tg.TG_OK or not kname.endswith("_pers_dma"):
+        print(f"bench.py --xcd-times: {w.name} does not plan to the persistent kernel ({kname})", file=sys.stderr)
+        return 2
+    _, cus, _, arch = tg.tg_device_info()
+    per_call = 3 * max(cus, 8)
+    stamps = torch.full((args.steps * per_call,), -1, dtype=torch.int64, device=dev)
+    for i in range(args.warmup):
+        A, B, D = sets[i % 2]
+        if tg.tg_gemm_f16(A, B, D, w.M, w.N, w.K, w.K, w.K, w.N, stream) != tg.TG_OK:
+            raise RuntimeError("tg_gemm_f16 failed")
+    wgs = set()
+    for i in range(args.steps):
+        A, B, D = sets[i % 2]
+        st, wg = tg.tg_gemm_f16_xcd_stamps(A, B, D, w.M, w.N, w.K, w.K, w.K, w.N,
+                                           stamps.data_ptr() + 8 * i * per_call, per_call, stream)
+        if st != tg.TG_OK:
+            raise RuntimeError(f"tg_gemm_f16_xcd_stamps: {tg.tg_status_string(st)}")
+        wgs.add(wg)
+    torch.cuda.synchronize(dev)
+    if len(wgs) != 1:
+        raise RuntimeError(f"workgroup counts differ between calls: {sorted(wgs)}")
+    wg = wgs.pop()
+    s = stamps.view(args.steps, per_call)[:, :3 * wg].reshape(args.steps, wg, 3).cpu().numpy()
+    start, end, xcc = s[:, :, 0], s[:, :, 1], s[:, :, 2]
+    if (end < start).any() or (xcc < 0).any() or (xcc >= 8).any():
+        raise RuntimeError("stamps out of range")
+    t0 = start.min(axis=1, keepdims=True)
+    ends_us = (end - t0) / 100.0  # 100 MHz clock
+    xcd_end = np.stack([np.where(xcc == x, ends_us, -np.inf).max(axis=1) for x in range(8)], axis=1)
+    wg_per_xcd = [int((xcc[0] == x).sum()) for x in range(8)]
+    span = xcd_end.max(axis=1)
+    mean_end = xcd_end.mean(axis=1)
+    late = (span - mean_end) / span
+    slowest = np.bincount(xcd_end.argmax(axis=1), minlength=8)
+    line = {"metric": "per-XCD end of the persistent fp16 GEMM (tg_gemm_f16_xcd_stamps)", "unit": "us",
+            "workload": w.name, "kernel": kname, "tiles": tiles, "workgroups": wg, "workgroups_per_xcd": wg_per_xcd,
+            "steps": args.steps, "warmup": args.warmup,
+            "xcd_mean_end_us": [round(float(v), 1) for v in xcd_end.mean(axis=0)],
+            "mean_span_us": round(float(span.mean()), 1), "mean_xcd_end_us": round(float(mean_end.mean()), 1),
+            "late_share": round(float(late.mean()), 4), "slowest_xcd_counts": [int(v) for v in slowest],
+            "workgroup_w_on_xcd_w_mod_8": bool(np.all(xcc == np.arange(wg) % 8)),
+            "wg_end_spread_within_xcd_us": round(float(np.mean([
+                (np.where(xcc == x, ends_us, -np.inf).max(axis=1) - np.where(xcc == x, ends_us, np.inf).min(axis=1)).mean()
+                for x in range(8)])), 1),
+            "device": {"arch": arch, "compute_units": cus}}
+    log(f"{w.name} {kname}: span {line['mean_span_us']} us, mean XCD end {line['mean_xcd_end_us']} us, "
+        f"late share {100 * line['late_share']:.1f}%, XCD ends {line['xcd_mean_end_us']}")
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def algorithmic_bytes(w, dtype: str) -> int:
     """Compulsory HBM bytes of one call: A and B read once, D (fp16) written once;
     the block-scaled entry point reads 1-byte codes plus one scale byte per 32 K
@@ -558,6 +632,8 @@ def main() -> int:
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only time the matrix-core stream (tg_mfma_ceiling) on the workload's A and B "
                          "and on zeros, for both MFMA shapes; one JSON line")
+    ap.add_argument("--xcd-times", action="store_true",
+                    help="per-XCD end times of the persistent fp16 kernel on --workload (measurement only)")
     ap.add_argument("--hbm-ceiling", action="store_true",
                     help="only time a streaming read of HBM (tg_hbm_read_ceiling) over two alternating "
                          "1 GiB buffers; one JSON line")
@@ -609,7 +685,7 @@ def main() -> int:
         return traffic_record(args)
 
     if args.processes > 1:
-        if args.all or args.mfma_ceiling or args.hbm_ceiling or args.copy_bytes:
+        if args.all or args.mfma_ceiling or args.hbm_ceiling or args.xcd_times or args.copy_bytes:
             print("--processes applies to the single benchmark line only", file=sys.stderr)
             return 2
         return run_processes(args)
@@ -637,6 +713,8 @@ def main() -> int:
         return mfma_ceiling(w, args)
     if args.hbm_ceiling:
         return hbm_ceiling(args)
+    if args.xcd_times:
+        return xcd_times(w, args)
 
     if args.all:
         pk = PEAK_FP8_TFLOPS if args.dtype == "mxf8" else PEAK_FP16_TFLOPS

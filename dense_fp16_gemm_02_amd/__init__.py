@@ -27,7 +27,8 @@ __all__ = ["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_LAUNCH", "TG_ERR_DEVICE", "TG_
            "TG_MX_E4M3", "TG_MX_E5M2", "tg_gemm_mx", "tg_gemm_mx_plan", "tg_gemm_mx_packed",
            "tg_gemm_mx_packed_plan",
            "TgError", "lib_path", "load", "tg_gemm_f16", "tg_gemm_f16_plan", "tg_gemm_bf16",
-           "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "tg_mfma_ceiling", "tg_hbm_read_ceiling", "gemm"]
+           "tg_gemm_bf16_plan", "tg_status_string", "tg_device_info", "tg_mfma_ceiling", "tg_hbm_read_ceiling",
+           "tg_gemm_f16_xcd_stamps", "gemm"]
 
 TG_MX_E4M3 = 0  # block-scaled element encodings (include/tg_gemm.h)
 TG_MX_E5M2 = 1
@@ -107,6 +108,8 @@ def load():
                                     ctypes.c_int, vp, vp]
     lib.tg_hbm_read_ceiling.restype = ctypes.c_int
     lib.tg_hbm_read_ceiling.argtypes = [vp, i64, ctypes.c_int, vp, vp]
+    lib.tg_gemm_f16_xcd_stamps.restype = ctypes.c_int
+    lib.tg_gemm_f16_xcd_stamps.argtypes = [vp, vp, vp] + [i64] * 6 + [vp, i64, ctypes.POINTER(i64), vp]
     lib.tg_device_info.restype = ctypes.c_int
     lib.tg_device_info.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                    ctypes.c_char_p, i64]
@@ -251,6 +254,17 @@ def tg_hbm_read_ceiling(src, nbytes: int, workgroups: int, out, stream=None) -> 
     """Enqueue one streaming read of nbytes at src (measurement only; see
     include/tg_ceiling.h); returns the C status code."""
     return load().tg_hbm_read_ceiling(_ptr(src), nbytes, workgroups, _ptr(out), _stream(stream))
+
+
+def tg_gemm_f16_xcd_stamps(A, B, D, M: int, N: int, K: int, lda: int, ldb: int, ldd: int, stamps,
+                           stamps_len: int, stream=None):
+    """tg_gemm_f16 through the stamping persistent kernel (measurement only;
+    see include/tg_ceiling.h): (status, workgroups launched).  stamps: device
+    buffer of stamps_len 64-bit words, three per workgroup."""
+    wg = ctypes.c_int64(0)
+    st = load().tg_gemm_f16_xcd_stamps(_ptr(A), _ptr(B), _ptr(D), M, N, K, lda, ldb, ldd, _ptr(stamps),
+                                       stamps_len, ctypes.byref(wg), _stream(stream))
+    return st, wg.value
 
 
 def tg_status_string(status: int) -> str:

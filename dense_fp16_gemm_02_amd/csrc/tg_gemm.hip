@@ -1396,12 +1396,26 @@ __global__ __launch_bounds__(WM *WN * 64) TG_WAVES_PER_SIMD(1) void gemm_dma3_ke
 //
 // RS0: fragment reads of K-step 0 every RS0-th MFMA slot (2: in the first
 // half of the step, so they have landed by the barrier's wait; 4: spread).
-template <typename E, int SA_, int GM, int RS0>
+//
+// STAMP (measurement only, tg_gemm_f16_xcd_stamps): the same kernel, plus
+// three words per workgroup in `stamps` — the constant 100 MHz clock when it
+// starts and when all its waves are done, and the XCD it ran on.  The GEMM
+// launch passes a null `stamps` and never reads it.
+template <typename E, int SA_, int GM, int RS0, bool STAMP = false>
 __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
     const E *__restrict__ A, const E *__restrict__ B, E *__restrict__ D,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldd, int tiles_m, int tiles_n,
-    int dvec)
+    int dvec, unsigned long long *__restrict__ stamps)
 {
+    if constexpr (STAMP) {
+        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+        unsigned xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        if (threadIdx.x == 0) {
+            stamps[3 * blockIdx.x] = t0;
+            stamps[3 * blockIdx.x + 2] = xcc;
+        }
+    }
     using V8 = typename Elem<E>::v8;
     using V4 = typename Elem<E>::v4;
     constexpr int BM = 256, BN = 256, WM = 2, WN = 2, MF = 16, BK_ = 64;
@@ -1675,6 +1689,12 @@ __global__ __launch_bounds__(256) TG_WAVES_PER_SIMD(1) void gemm_pers_kernel(
         fresh = true;
     }
     wait_vmem<0>();  // no DMA or store may be outstanding when the wave ends
+    if constexpr (STAMP) {
+        barrier_lds();  // every wave is done
+        const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+        if (threadIdx.x == 0)
+            stamps[3 * blockIdx.x + 1] = t1;
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -2682,10 +2702,45 @@ int launch(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t 
         return TG_ERR_TOO_LARGE;
     const int64_t grid = p.k.persistent ? persistent_grid(tiles) : tiles;
     int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+    unsigned long long *no_stamps = nullptr;  // the persistent kernel's last argument; others take 12
     void *args[] = {(void *)&A, (void *)&B, (void *)&D, &Mi, &Ni, &Ki, &lda, &ldb, &ldd,
-                    &p.tiles_m, &p.tiles_n, &p.dvec};
+                    &p.tiles_m, &p.tiles_n, &p.dvec, &no_stamps};
     hipError_t e = hipLaunchKernel(p.k.fn, dim3((unsigned)grid), dim3(p.k.threads), args, 0,
                                    (hipStream_t)stream);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+// The fp16 GEMM through the stamping instantiation of the persistent kernel
+// (measurement only): the plan must be the persistent one, and `stamps`
+// must hold three words per workgroup.
+int launch_stamped(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, int64_t lda,
+                   int64_t ldb, int64_t ldd, uint64_t *stamps, int64_t stamps_len, int64_t *workgroups,
+                   void *stream)
+{
+    if (workgroups)
+        *workgroups = 0;
+    int st = validate(A, B, D, M, N, K, lda, ldb, ldd);
+    if (st != TG_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return TG_ERR_INVALID_ARG;
+    Plan p = make_plan<_Float16>(A, B, D, M, N, K, lda, ldb, ldd);
+    if (!p.k.persistent)
+        return TG_ERR_INVALID_ARG;
+    const int64_t grid = persistent_grid((int64_t)p.tiles_m * p.tiles_n);
+    if (!stamps || stamps_len < 3 * grid)
+        return TG_ERR_INVALID_ARG;
+    st = check_device();
+    if (st != TG_OK)
+        return st;
+    if (workgroups)
+        *workgroups = grid;
+    int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+    unsigned long long *sp = reinterpret_cast<unsigned long long *>(stamps);
+    void *args[] = {(void *)&A, (void *)&B, (void *)&D, &Mi, &Ni, &Ki, &lda, &ldb, &ldd,
+                    &p.tiles_m, &p.tiles_n, &p.dvec, &sp};
+    const void *fn = reinterpret_cast<const void *>(&gemm_pers_kernel<_Float16, TG_P_SA, TG_P_GM, TG_P_RS0, true>);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
@@ -2714,6 +2769,13 @@ extern "C" int tg_gemm_f16(const void *A, const void *B, void *D, int64_t M, int
                            int64_t K, int64_t lda, int64_t ldb, int64_t ldd, void *stream)
 {
     return launch<_Float16>(A, B, D, M, N, K, lda, ldb, ldd, stream);
+}
+
+extern "C" int tg_gemm_f16_xcd_stamps(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
+                                      int64_t lda, int64_t ldb, int64_t ldd, uint64_t *stamps, int64_t stamps_len,
+                                      int64_t *workgroups, void *stream)
+{
+    return launch_stamped(A, B, D, M, N, K, lda, ldb, ldd, stamps, stamps_len, workgroups, stream);
 }
 
 extern "C" int tg_gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N,

@@ -12,7 +12,10 @@
  * throughput; this gives that throughput on this part, for the operand data
  * the GEMM sees).
  *
- * Not part of the GEMM path: the GEMM never calls it.
+ * Also a stamping form of the persistent fp16 GEMM that records when each
+ * workgroup starts and ends and on which XCD it runs.
+ *
+ * Not part of the GEMM path: the GEMM never calls these.
  */
 #ifndef TG_CEILING_H
 #define TG_CEILING_H
@@ -74,6 +77,35 @@ int tg_mfma_ceiling(int shape, const void *A, int64_t a_elems, const void *B, in
  * TG_ERR_INVALID_ARG or TG_ERR_LAUNCH.  Asynchronous.
  */
 int tg_hbm_read_ceiling(const void *src, int64_t bytes, int workgroups, unsigned *out, void *stream);
+
+/*
+ * tg_gemm_f16_xcd_stamps — tg_gemm_f16 for a problem that plans to the
+ * persistent 256x256 kernel ("TIRx 与高性能GEMM (上)", Step 6: a fixed pool
+ * of workgroups that keeps taking tiles), through an instantiation of that
+ * kernel that also records, per workgroup, when it started and when all its
+ * waves were done (the constant 100 MHz clock of s_memrealtime) and the XCD
+ * it ran on.  D is what tg_gemm_f16 writes, bit for bit.  The spread of the
+ * XCDs' last end times shows how much of a launch is one XCD finishing
+ * after the others under the static tile schedule.
+ *
+ *   A, B, D, M, N, K, lda, ldb, ldd   as for tg_gemm_f16.
+ *   stamps      device pointer to stamps_len 64-bit words; workgroup w
+ *               writes words 3w (start), 3w + 1 (end), 3w + 2 (XCD id).
+ *   stamps_len  at least 3 x the workgroup count (the compute-unit count
+ *               rounded down to a multiple of 8, at most the tile count).
+ *   workgroups  host pointer (may be NULL): the workgroup count launched.
+ *   stream      hipStream_t (NULL: the null stream).
+ *
+ * Returns TG_OK; TG_ERR_INVALID_ARG when the arguments fail tg_gemm_f16's
+ * checks, M or N is 0, the problem does not plan to the persistent kernel,
+ * or stamps is NULL or too short (nothing launched); TG_ERR_TOO_LARGE,
+ * TG_ERR_DEVICE or TG_ERR_LAUNCH as for tg_gemm_f16.  Asynchronous; calls
+ * that overlap must not share a stamps buffer.  Measurement only: the GEMM
+ * path never calls it.
+ */
+int tg_gemm_f16_xcd_stamps(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
+                           int64_t lda, int64_t ldb, int64_t ldd, uint64_t *stamps, int64_t stamps_len,
+                           int64_t *workgroups, void *stream);
 
 #ifdef __cplusplus
 }

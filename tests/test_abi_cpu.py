@@ -268,3 +268,18 @@ def test_packed_scale_entry_points_validation():
     assert tg.tg_mx_pack_scales(FAKE, 4, 128, 4, FAKE + 4, None) == tg.TG_ERR_LAYOUT
     assert tg.tg_mx_pack_scales(FAKE, 1 << 31, 128, 4, FAKE, None) == tg.TG_ERR_TOO_LARGE
     assert tg.tg_mx_pack_scales(None, 0, 128, 4, None, None) == tg.TG_OK
+
+
+def test_xcd_stamps_validation():
+    """The stamping entry point runs only problems that plan to the
+    persistent kernel, with room for three words per workgroup; everything
+    else is refused before a device is touched."""
+    M, N, K = 8192, 14336, 4096  # persistent: 1792 tiles, at most 256 workgroups
+    big = 3 * 4096
+    for kw in [dict(M=128, N=128, K=64), dict(M=1000, N=1000, K=1000), dict(M=4096, N=4096, K=4096),
+               dict(K=4000), dict(stamps=None), dict(stamps_len=3), dict(M=0), dict(M=-1), dict(lda=8)]:
+        p = {**dict(M=M, N=N, K=K, lda=None, stamps=FAKE, stamps_len=big), **kw}
+        lda = p["lda"] if p["lda"] is not None else p["K"]
+        st, wg = tg.tg_gemm_f16_xcd_stamps(FAKE, FAKE, FAKE, p["M"], p["N"], p["K"], lda, p["K"], p["N"],
+                                           p["stamps"], p["stamps_len"])
+        assert st == tg.TG_ERR_INVALID_ARG and wg == 0, kw
