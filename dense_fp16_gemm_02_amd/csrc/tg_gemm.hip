@@ -2409,11 +2409,17 @@ struct KernelChoice {
 #ifndef TG_M_STAGES
 #define TG_M_STAGES 4
 #endif
+// The 64×64 tile takes 128-K tiles in three stages (32 KiB each): its small
+// MFMA work per K-tile left the K loop bound by the per-K-tile wait and
+// barrier, and halving their number measured 4–11% faster than 64-K tiles
+// in four stages (64×3584×8192 30.3 → 26.9 µs, 32×4096×4096 16.4 → 14.8,
+// 1000²×4096 19.3 → 17.2, 1000³ 6.94 → 6.65, 1024³ 6.45 → 6.12; one box),
+// while deeper 64-K rings (6–10 stages) measured no better.
 #ifndef TG_S_BK
-#define TG_S_BK 64
+#define TG_S_BK 128
 #endif
 #ifndef TG_S_STAGES
-#define TG_S_STAGES 4
+#define TG_S_STAGES 3
 #endif
 #ifndef TG_S_KROT
 #define TG_S_KROT 0
