@@ -41,7 +41,8 @@ class Case:
 
 
 # (tile, path) -> Case.  The integer patterns keep sums exact: the fp16 index
-# pattern needs K <= 341, the bf16 {-1, 0, 1} pattern K <= 256.
+# pattern for K <= 341, else {-1, 0, 1} (|D| <= K <= 2048); the bf16 {-1, 0, 1}
+# pattern, whose fp32 sums stay exact integers, rounded once on both sides.
 _F16_BF16 = {
     # column strips, M <= 64 / 128 / 256 with at least 128 strips of 128 columns
     ("64x128_w1x4", "dma"): Case(37, 16411, 200),
@@ -65,6 +66,8 @@ _F16_BF16 = {
     ("128x128_w2x2_ws", "dma"): Case(2100, 2000, 200),
     ("128x128_w2x2", "vec"): Case(129, 5120, 64, lda=vec_lda(128)),
     ("128x128_w2x2", "scalar"): Case(1000, 2000, 250),
+    # 64x32 on the direct-to-LDS path: at most 128 tiles of 64x64 and K >= 2048
+    ("64x32_w2x2", "dma"): Case(64, 3584, 2048),
     ("64x64_w2x2", "dma"): Case(1000, 1000, 200),
     ("64x64_w2x2", "vec"): Case(2, 300, 64, lda=17_100_000),
     ("64x64_w2x2", "scalar"): Case(97, 131, 250),
@@ -98,7 +101,7 @@ MXF_CASES: dict[str, tuple] = {
 
 TILES = sorted({t for t, _ in _F16_BF16})
 PATHS = ("dma", "vec", "scalar")
-DMA_ONLY = {"256x256_w2x2_pers", "128x128_w2x2_ws"}  # kernels only on the direct-to-LDS path
+DMA_ONLY = {"256x256_w2x2_pers", "128x128_w2x2_ws", "64x32_w2x2"}  # kernels only on the direct-to-LDS path
 NO_DMA = {"128x128_w2x2"}  # kernels whose direct-to-LDS form is another kernel
 
 

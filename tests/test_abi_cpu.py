@@ -100,7 +100,8 @@ def test_plans_for_workloads():
     (1, 16385, 64, "64x128", 129),
     (128, 28672, 8192, "128x128", 224),
     (256, 28672, 8192, "256x128", 224),
-    (64, 4096, 8192, "64x64", 64),        # too few strips to fill the chip
+    (64, 4096, 8192, "64x32", 128),       # too few strips to fill the chip; long K: 64x32 tiles
+    (64, 4096, 1024, "64x64", 64),        # the same with short K
     (8192, 14336, 4096, "256x256", 1792),
     (4096, 4096, 4096, "256x256", 256),
     (2048, 2048, 2048, "128x128", 256),

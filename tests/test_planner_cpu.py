@@ -52,7 +52,7 @@ def test_planner_sweep_stays_inside_the_table():
     Ns = [131, 300, 2000, 5120, 16256, 16385, 16411, 40960]
     seen = set()
     for fmt, M, N in itertools.product(("f16", "bf16"), Ms, Ns):
-        for K, a_off in ((64, 0), (128, 0), (200, 0), (250, 0), (96, 1)):
+        for K, a_off in ((64, 0), (128, 0), (200, 0), (250, 0), (96, 1), (2048, 0)):
             for lda in (K, vec_lda(256), vec_lda(128), vec_lda(64)):
                 name = _plan(fmt, M, N, K, lda, K, a_off)
                 assert name in CASES, (fmt, M, N, K, lda, a_off, name)
