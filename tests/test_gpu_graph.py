@@ -57,11 +57,12 @@ def _replays_match(call, D, label, replays=4):
 @pytest.mark.parametrize("M,N,K,name", [(4096, 8192, 512, "gemm_f16_256x256_w2x2_pers_dma"),
                                         (2100, 2000, 200, "gemm_f16_128x128_w2x2_ws_dma"),
                                         (64, 16411, 200, "gemm_f16_64x128_w1x4_dma"),
+                                        (64, 3584, 2048, "gemm_f16_64x32_w2x2_dma"),
                                         (97, 131, 250, "gemm_f16_64x64_w2x2_scalar")])
 def test_fp16_call_replays_in_a_graph(M, N, K, name):
     st, planned, _ = tg.tg_gemm_f16_plan(1 << 20, 1 << 20, 1 << 20, M, N, K, K, K, N)
     assert st == tg.TG_OK and planned == name
-    a, b = workloads.small_int_pattern(M, N, K)
+    a, b = workloads.small_int_pattern(M, N, K)  # |D| <= K <= 2048: exact in binary16
     A = torch.from_numpy(a).to("cuda:0")
     B = torch.from_numpy(b).to("cuda:0")
     D = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
